@@ -1,0 +1,197 @@
+"""Oracle for the per-layer n-gram embedding (PLE) lookup path.
+
+TEST INFRASTRUCTURE ONLY: the plain, slow, single-threaded CPU statement of
+what the path computes (C in ``ple_oracle.c``, compiled with gcc, no HIP).
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package; the GPU library shares no code with it and never calls
+it.  Each function cites the page passage it follows in ``ple_oracle.h``.
+
+The wrappers below marshal numpy arrays; ``prefill`` runs the stages in the
+order the pages give them (ids, row lookup, merged kv_proj, gate, conv).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from functools import lru_cache
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libple_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    src = os.path.join(_HERE, "ple_oracle.c")
+    hdr = os.path.join(_HERE, "ple_oracle.h")
+    stale = (not os.path.exists(_LIB_PATH) or
+             os.path.getmtime(_LIB_PATH) < max(os.path.getmtime(src), os.path.getmtime(hdr)))
+    if force or stale:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+@lru_cache(maxsize=1)
+def _lib():
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.orc_ngram_ids.argtypes = [P, P, I64, I32, P, I32, I32, I32, I32, I32, P, P, P, P, P]
+    lib.orc_ngram_ids.restype = ctypes.c_int
+    lib.orc_gather_bf16.argtypes = [P, I32, P, I64, P]
+    lib.orc_gather_fp8.argtypes = [P, P, I32, P, I64, P]
+    lib.orc_e4m3fn_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3fn_value.restype = D
+    lib.orc_bf16_from_double.argtypes = [D]
+    lib.orc_bf16_from_double.restype = ctypes.c_uint16
+    lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_value.restype = D
+    lib.orc_kv_proj.argtypes = [P, P, I64, I32, I32, P]
+    lib.orc_gate.argtypes = [P, P, I64, I32, D, P, P]
+    lib.orc_conv.argtypes = [P, P, I64, I32, P, P, I32, I32, I32, P, P]
+    lib.orc_conv.restype = ctypes.c_int
+    return lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle takes C-contiguous numpy arrays"
+    return a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def ngram_ids(input_ids, qsl, multipliers, vocab_sizes, offsets, *, context_len, heads_per_ngram,
+              eos_token_id, ngram_context=None, first_head=0, num_heads=None, want_context_out=False):
+    """IDs int32 [T, H] (and the carried context [R, C] if asked)."""
+    tok = _c(input_ids, np.int32)
+    q = _c(qsl, np.int32)
+    mult = _c(multipliers, np.int64)
+    V = _c(vocab_sizes, np.int64)
+    off = _c(offsets, np.int64)
+    ctx = _c(ngram_context, np.int32)
+    H = len(V) if num_heads is None else num_heads
+    T, R = tok.shape[0], q.shape[0] - 1
+    assert mult.shape == (H, context_len + 1)
+    ids = np.empty((T, H), dtype=np.int32)
+    ctx_out = np.empty((R, context_len), dtype=np.int32) if want_context_out else None
+    rc = _lib().orc_ngram_ids(_p(tok), _p(q), T, R, _p(ctx), context_len, heads_per_ngram, first_head, H,
+                              eos_token_id, _p(mult), _p(V), _p(off), _p(ids), _p(ctx_out))
+    if rc:
+        raise ValueError("oracle ngram_ids: argument out of range")
+    return (ids, ctx_out) if want_context_out else ids
+
+
+def gather_bf16(table, ids):
+    """rows [n, D] (bf16 bits) = table[ids]."""
+    ids = _c(ids, np.int32).reshape(-1)
+    D = table.shape[1]
+    rows = np.empty((ids.shape[0], D), dtype=np.uint16)
+    _lib().orc_gather_bf16(_p(table), D, _p(ids), ids.shape[0], _p(rows))
+    return rows
+
+
+def gather_fp8(codes, scales, ids):
+    ids = _c(ids, np.int32).reshape(-1)
+    D = codes.shape[1]
+    rows = np.empty((ids.shape[0], D), dtype=np.uint16)
+    _lib().orc_gather_fp8(_p(codes), _p(scales), D, _p(ids), ids.shape[0], _p(rows))
+    return rows
+
+
+def e4m3fn_value(code: int) -> float:
+    return _lib().orc_e4m3fn_value(code)
+
+
+def bf16_from_double(x: float) -> int:
+    return _lib().orc_bf16_from_double(x)
+
+
+def bf16_value(bits: int) -> float:
+    return _lib().orc_bf16_value(bits)
+
+
+def kv_proj(x, w):
+    """kv [T, O] (bf16 bits) = bf16(x @ w.T) with double accumulation."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    T, K = x.shape
+    O = w.shape[0]
+    assert w.shape[1] == K
+    kv = np.empty((T, O), dtype=np.uint16)
+    _lib().orc_kv_proj(_p(x), _p(w), T, K, O, _p(kv))
+    return kv
+
+
+def gate(hidden, kv, eps=1e-6):
+    """(out [T, N] bf16 bits, g [T] float64)."""
+    hidden = _c(hidden, np.uint16)
+    kv = _c(kv, np.uint16)
+    T, N = hidden.shape
+    assert kv.shape == (T, 2 * N)
+    out = np.empty((T, N), dtype=np.uint16)
+    g = np.empty((T,), dtype=np.float64)
+    _lib().orc_gate(_p(hidden), _p(kv), T, N, eps, _p(out), _p(g))
+    return out, g
+
+
+def conv(x, qsl, w, dilation, state=None, want_state_out=False):
+    """y [T, N] (bf16 bits) and optionally the carried state [R, S, N]."""
+    x = _c(x, np.uint16)
+    q = _c(qsl, np.int32)
+    w = _c(w, np.uint16)
+    st = _c(state, np.uint16)
+    T, N = x.shape
+    K = w.shape[1]
+    R = q.shape[0] - 1
+    S = (K - 1) * dilation
+    y = np.empty((T, N), dtype=np.uint16)
+    so = np.empty((R, S, N), dtype=np.uint16) if want_state_out else None
+    rc = _lib().orc_conv(_p(x), _p(q), T, R, _p(st), _p(w), N, K, dilation, _p(y), _p(so))
+    if rc:
+        raise ValueError("oracle conv: argument out of range")
+    return (y, so) if want_state_out else y
+
+
+def prefill(batch_ids_args: dict, table, scales, hidden, kv_weight, conv_weight, dilation, *,
+            qsl, eps=1e-6, conv_state=None, tokens=None):
+    """Whole path: ids -> rows -> kv -> gate -> conv.
+
+    ``tokens`` (optional, sorted) restricts kv_proj to the listed tokens and the
+    conv taps they need; outputs at other tokens are then meaningless, and the
+    caller compares only the listed ones.  Returns a dict of every stage.
+    """
+    ids = ngram_ids(**batch_ids_args)
+    T, H = ids.shape
+    rows = gather_bf16(table, ids) if scales is None else gather_fp8(table, scales, ids)
+    rows = rows.reshape(T, -1)
+    if tokens is None:
+        kv = kv_proj(rows, kv_weight)
+    else:
+        need = conv_taps(tokens, qsl, conv_weight.shape[1], dilation)
+        kv = np.zeros((T, kv_weight.shape[0]), dtype=np.uint16)
+        kv[need] = kv_proj(rows[need], kv_weight)
+    out, g = gate(hidden, kv, eps)
+    y = conv(out, qsl, conv_weight, dilation, state=conv_state)
+    return {"ids": ids, "rows": rows, "kv": kv, "gated": out, "gate": g, "y": y}
+
+
+def conv_taps(tokens, qsl, kernel, dilation):
+    """Sorted token indices that the conv outputs at `tokens` read (same request only)."""
+    q = np.asarray(qsl, dtype=np.int64)
+    need = set()
+    for t in np.asarray(tokens, dtype=np.int64):
+        r = int(np.searchsorted(q, t, side="right") - 1)
+        for i in range(kernel):
+            p = int(t) - i * dilation
+            if p >= q[r]:
+                need.add(p)
+    return np.asarray(sorted(need), dtype=np.int64)
