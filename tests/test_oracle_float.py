@@ -285,3 +285,31 @@ def test_conv_state_out_for_short_and_empty_requests():
     np.testing.assert_array_equal(so[0], st_in[0])                       # empty: unchanged
     np.testing.assert_array_equal(so[1], np.concatenate([st_in[1][2:], x[0:2]]))
     np.testing.assert_array_equal(so[2], np.concatenate([st_in[2][1:], x[2:3]]))
+
+
+def _float_neighbours(x: float, n: int):
+    f = np.float32(x)
+    out = [f]
+    up = dn = f
+    for _ in range(n):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(-np.inf))
+        out += [up, dn]
+    return out
+
+
+def test_gather_fp8_multiply_rounds_in_fp32_first():
+    # A product just below a bf16 midpoint whose fp32 rounding lands on the midpoint:
+    # one fp32 multiply then RNE gives the even (upper) bf16, direct rounding the lower.
+    v = Fraction(9, 8)                       # code 0x39 = 1.125
+    mid = Fraction(1) + Fraction(3, 256)     # midpoint of bf16 0x3F81 and 0x3F82
+    found = None
+    for s in _float_neighbours(float(mid / v), 64):
+        exact = v * Fraction(float(s))
+        if exact < mid and Fraction(float(np.float32(9 / 8) * s)) == mid:
+            found = s
+            break
+    assert found is not None
+    got = oracle.gather_fp8(np.asarray([[0x39]], np.uint8), np.asarray([found], np.float32),
+                            np.asarray([0], np.int32))
+    assert got[0, 0] == 0x3F82
