@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-layer n-gram embedding (PLE) hot path on one MI355X.
+
+Default workload: 8192-token prefill over ragged requests (geometric lengths,
+mean 512, clipped to [1, 4096]) with Zipf(1.1) token ids, 8 hash heads (orders
+2 and 3) over an 8.39M-row x 512 bf16 table in HBM, hidden 4096, kv_proj
+4096 -> 2x4096, gate, and conv (kernel 4, dilation 3).  One step is one pass of
+the whole path for one layer: fused ids+gather, kv_proj, gate, conv.  Steps
+rotate over 16 layers' hash multipliers (and 4 kv weights) so consecutive
+lookups touch different rows (about 1 GB of distinct rows per 16 steps, more
+than the 256 MB last-level cache).
+
+Prints one JSON line (rank 0): tokens/s of the whole path, per-stage times
+from HIP events on the launch stream, the dominant kernel's roofline, the
+fused lookup's gathered GB/s, and the single-threaded CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s + gathered GB/s (% HBM peak), fused PLE lookup, 8k-token prefill"
+HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=16, help="hash layers rotated over the steps")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import layer_embedding_lookup_amd as ple
+    import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = wl.CONFIGS[3]
+    L = args.layers
+    log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} rows={cfg.num_rows} D={cfg.D} N={cfg.N}")
+    b = wl.make_batch(cfg, layers=L)
+    log("generating the table on the host")
+    t0 = time.time()
+    table_h, _ = wl.make_table(cfg)
+    log(f"table ready in {time.time() - t0:.1f}s; copying to HBM")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def it(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    table = bf(table_h)
+    kv_ws_h = [wl.make_kv_weight(cfg, layer=i) for i in range(4)]
+    kv_ws = [bf(w) for w in kv_ws_h]
+    conv_w_h = wl.make_conv_weight(cfg)
+    conv_w = bf(conv_w_h)
+    hidden_h = wl.make_hidden(cfg)
+    hidden = bf(hidden_h)
+    toks, qsl = it(b.input_ids), it(b.qsl)
+    tb = ple.Table.from_tensor(table)
+    hashes = [ple.HashParams(b.multipliers[l], b.vocab_sizes, b.offsets, heads_per_ngram=cfg.heads_per_ngram,
+                             context_len=cfg.context_len, eos_token_id=wl.EOS) for l in range(L)]
+    layers = [ple.Layer(hashes[l], tb, kv_ws[l % 4], conv_w, conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+              for l in range(L)]
+    T, H, D, N = cfg.T, cfg.H, cfg.D, cfg.N
+    rows = torch.empty((T, H * D), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((T, 2 * N), dtype=torch.bfloat16, device=dev)
+    gated = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((ple.ple_prefill_workspace_bytes(layers[0], T),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s, evs=None):
+        lay = layers[s % L]
+        if evs is not None:
+            evs[0].record()
+        ple.ple_lookup(lay.hash, lay.table, toks, qsl, rows=rows)
+        if evs is not None:
+            evs[1].record()
+        ple.ple_kv_proj(rows, lay.kv_weight, kv=kv)
+        if evs is not None:
+            evs[2].record()
+        ple.ple_gate(hidden, kv, eps=lay.eps, out=gated, want_gate=False)
+        if evs is not None:
+            evs[3].record()
+        ple.ple_conv(gated, qsl, lay.conv_weight, dilation=lay.conv_dilation, y=out)
+        if evs is not None:
+            evs[4].record()
+
+    log(f"warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / K
+    stage_names = ["lookup", "kv_proj", "gate", "conv"]
+    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)]))
+                for i, n in enumerate(stage_names)}
+    gpu_step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][4]) for s in range(K)]))
+
+    # the same path through the single fused entry point
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    for s in range(K):
+        lay = layers[(args.warmup + s) % L]
+        ple.ple_prefill_fused(lay, toks, qsl, hidden, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - tf0) * 1e3 / K
+
+    # lookup alone: 16 back-to-back launches over different layers (cold last-level cache)
+    lk = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 4
+    torch.cuda.synchronize()
+    lk[0].record()
+    for r in range(reps):
+        for l in range(L):
+            ple.ple_lookup(hashes[l], tb, toks, qsl, rows=rows)
+    lk[1].record()
+    torch.cuda.synchronize()
+    lookup_ms = lk[0].elapsed_time(lk[1]) / (reps * L)
+
+    R = b.R
+    lookup_bytes = T * H * D * 2 * 2 + T * 4 + (R + 1) * 4
+    lookup_gbps = lookup_bytes / (lookup_ms * 1e-3) / 1e9
+    kv_flops = 2.0 * T * (H * D) * (2 * N)
+    kv_tflops = kv_flops / (stage_ms["kv_proj"] * 1e-3) / 1e12
+    gate_bytes = T * N * 2 * 4   # hidden + key + value read, gated value written
+    conv_bytes = T * N * 2 * 2   # x read once, y written
+    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, b, table_h, kv_ws_h[0], conv_w_h, hidden_h, args.cpu_sample_tokens)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "requests": R, "heads": H, "orders": [2, 3],
+                   "table_rows": cfg.num_rows, "dim": D, "table_dtype": "bf16", "table_location": "hbm",
+                   "hidden": N, "kv_proj": [H * D, 2 * N], "conv": [cfg.conv_kernel, cfg.conv_dilation],
+                   "layers_rotated": L},
+        "roofline": {"kernel": "kv_proj (MFMA bf16 GEMM)", "bound": "mfma",
+                     "achieved": round(kv_tflops, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kv_tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None},
+        "lookup": {"kernel": "fused ids+gather", "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
+                   "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
+                   "tokens_per_s": round(T / (lookup_ms * 1e-3), 1)},
+        "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stages_GBps": {"gate": round(gate_bytes / (stage_ms["gate"] * 1e-3) / 1e9, 1),
+                        "conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)},
+        "gpu_step_ms_events": round(gpu_step_ms, 4),
+        "fused_entry_ms_per_step": round(fused_ms, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(cfg, b, table_h, kvw_h, conv_w_h, hidden_h, n_tokens):
+    """The oracle, single-threaded, on a bounded sample: the first n_tokens of
+    request 0 (a prefix chunk) through the whole path."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    n = int(min(n_tokens, int(b.qsl[1])))
+    log(f"cpu baseline: oracle on the first {n} tokens of request 0 (whole path)")
+    ids_args = dict(input_ids=b.input_ids[:n], qsl=np.asarray([0, n], np.int32), multipliers=b.multipliers[0],
+                    vocab_sizes=b.vocab_sizes, offsets=b.offsets, context_len=cfg.context_len,
+                    heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS)
+    t0 = time.perf_counter()
+    oracle.prefill(ids_args, table_h, None, hidden_h[:n], kvw_h, conv_w_h, cfg.conv_dilation,
+                   qsl=np.asarray([0, n], np.int32), eps=cfg.eps)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} tokens of request 0 of the {cfg.name} batch, whole path "
+                      f"(ids, gather, kv_proj, gate, conv), single-threaded C, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

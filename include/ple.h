@@ -1,0 +1,245 @@
+/*
+ * ple.h - C ABI of libple, the MI355X (gfx950) per-layer n-gram embedding
+ * (PLE / Engram) lookup path.
+ *
+ * The path, per decoder layer, over a ragged batch of requests:
+ *   ple_ngram_ids  hash each token's preceding n-grams into per-head table rows
+ *   ple_gather     fetch one row per hash head (bf16 copy, or fp8 e4m3fn with a
+ *                  per-row fp32 scale dequantised to bf16)
+ *   ple_lookup     the two above fused into one kernel (the hot lookup)
+ *   ple_kv_proj    merged key/value projection (MFMA GEMM)
+ *   ple_gate       sigmoid gate of the RMS-normalised hidden.key product, times value
+ *   ple_conv       dilated causal depthwise short convolution
+ *   ple_prefill_fused  all of the above in stream order
+ *
+ * Sources (page title, then section):
+ *   [P1] "PR #54371 [Qwen4Exp] Support UVA PLE-offload and Engram tensor
+ *        parallelism": 功能与动机 (tables in pinned host memory read by the GPU
+ *        through unified addressing), 关键源码片段 (pinned allocation, side-stream
+ *        prefetch returning early on an empty batch).
+ *   [P2] "PR #56512 [DS V4.1][Engram] async prefetch for offloaded engram
+ *        lookups and engram DP sharding": 功能与动机 and 实现拆解 item 4
+ *        (side-stream prefetch into a persistent staging buffer; empty head
+ *        shards are rejected).
+ *   [P3] "PR #54517 [Qwen3.8-Flash-Next] Fuse Qwen4Exp PLE kernels": 实现拆解
+ *        items 1-2 (ids, gate and conv kernels; merged kv_proj) and 关键源码片段
+ *        (compute_ngram_ids and the ids kernel's arguments).
+ *   [P4] "Support PLE-Offload for Qwen3.8-Flash-Next - #53899": FP8
+ *        (float8_e4m3fn) PLE tables carrying a weight scale.
+ *
+ * Conventions for every call:
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - "device" pointers are HIP device addresses (hipMalloc, or the device
+ *     address of mapped pinned host memory where stated); "host" pointers are
+ *     read during the call only.  The caller owns all memory; the library
+ *     never allocates or frees on these paths.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     only enqueue work and never synchronise (except the host-memory calls).
+ *     Device buffers must stay alive until the enqueued work completes.
+ *   - Return value: PLE_OK or an error code; ple_error_message() describes
+ *     the last failure on the calling thread.  Argument checks run before any
+ *     HIP call, so an invalid call touches no device.  Nothing is thrown
+ *     across the ABI.
+ *   - Preconditions not checked on the device (violations give unspecified
+ *     results, never out-of-bounds table reads): query_start_loc[0] == 0,
+ *     non-decreasing, query_start_loc[R] == T; token ids >= 0.
+ *   - Tensors are row-major and densely packed; device pointers must be
+ *     16-byte aligned.
+ */
+#ifndef PLE_H
+#define PLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PLE_OK 0
+#define PLE_ERR_INVALID_ARGUMENT 1
+#define PLE_ERR_UNSUPPORTED 2
+#define PLE_ERR_DEVICE 3
+#define PLE_ERR_WORKSPACE 4
+
+#define PLE_DTYPE_BF16 0
+#define PLE_DTYPE_FP8_E4M3 1 /* OCP float8 e4m3fn: bias 7, max 448, NaN 0x7F/0xFF */
+
+#define PLE_MAX_HEADS 32
+#define PLE_MAX_CONTEXT 7
+
+/*
+ * Hash constants of one layer ([P3] 关键源码片段: layer multipliers, per-head
+ * vocabulary sizes and offsets, EOS id, heads per n-gram order).
+ * Orders are 2..context_len+1, order-major: global head g has order
+ * 2 + g / heads_per_ngram.  This call covers the global heads
+ * [first_head, first_head + num_heads) (a head shard; first_head = 0 and
+ * num_heads = context_len * heads_per_ngram for the whole layer).
+ */
+typedef struct ple_hash_desc {
+    int32_t num_heads;        /* H, 1..PLE_MAX_HEADS (0 is rejected: empty head shard) */
+    int32_t heads_per_ngram;  /* >= 1 */
+    int32_t context_len;      /* C = max order - 1, 1..PLE_MAX_CONTEXT */
+    int32_t first_head;       /* >= 0, first_head + num_heads <= C * heads_per_ngram */
+    int32_t eos_token_id;
+    int32_t reserved;
+    const int64_t* multipliers; /* host [H][C+1]; entry j of head h used for j < order(h) */
+    const int64_t* vocab_sizes; /* host [H]; 1 <= V_h < 2^31 */
+    const int64_t* offsets;     /* host [H]; >= 0; offsets[h] + V_h <= table rows and < 2^31 */
+} ple_hash_desc;
+
+/* An embedding table of one layer ([P1] 关键源码片段; [P4] FP8 tables). */
+typedef struct ple_table_desc {
+    const void* table;        /* device (or mapped host) [num_rows][dim] elements of dtype */
+    int64_t num_rows;         /* 1 .. 2^31 */
+    int32_t dim;              /* D; D*elem_size a multiple of 16 bytes, D <= 8192 */
+    int32_t dtype;            /* PLE_DTYPE_BF16 | PLE_DTYPE_FP8_E4M3 */
+    const float* row_scales;  /* fp8 only: device (or mapped host) [num_rows]; NULL for bf16 */
+} ple_table_desc;
+
+/*
+ * One ragged batch ([P3] 关键源码片段 compute_ngram_ids: flattened input_ids,
+ * query_start_loc with R+1 entries, the carried ngram_context).
+ */
+typedef struct ple_batch_desc {
+    const int32_t* input_ids;        /* device [T] */
+    const int32_t* query_start_loc;  /* device [R+1] */
+    int64_t num_tokens;              /* T >= 0 */
+    int32_t num_reqs;                /* R >= 0 (R == 0 requires T == 0) */
+    int32_t reserved;
+    const int32_t* ngram_context;    /* device [R][C], oldest first, or NULL (= all EOS) */
+    int32_t* ngram_context_out;      /* device [R][C] or NULL: last C raw tokens of
+                                        ngram_context[r] ++ request r's tokens; must not
+                                        alias ngram_context */
+    const uint16_t* conv_state;      /* device bf16 [R][S][N], oldest first, or NULL (= zeros);
+                                        S = (conv_kernel - 1) * conv_dilation */
+    uint16_t* conv_state_out;        /* device bf16 [R][S][N] or NULL; must not alias conv_state */
+} ple_batch_desc;
+
+/* Everything one layer's fused prefill needs. */
+typedef struct ple_layer_desc {
+    ple_hash_desc hash;
+    ple_table_desc table;
+    const uint16_t* kv_weight;   /* device bf16 [2N][H*D]: key rows, then value rows */
+    int32_t hidden;              /* N; a multiple of 8 */
+    float eps;                   /* RMS epsilon (1e-6 in the reference workloads) */
+    const uint16_t* conv_weight; /* device bf16 [N][Kc]; tap Kc-1 multiplies the current token */
+    int32_t conv_kernel;         /* Kc, 1..16 */
+    int32_t conv_dilation;       /* d >= 1, (Kc-1)*d <= 64 */
+} ple_layer_desc;
+
+/*
+ * N-gram IDs ([P3] 实现拆解 item 2, 关键源码片段).  For token t of request r
+ * (tokens [a, b) = [qsl[r], qsl[r+1])), shifts j = 0..C:
+ *   raw(0) = tok[t]; raw(j) = tok[t-j] if t-j >= a, else ngram_context[r][C-(a-(t-j))],
+ *   else EOS.  Once raw(j') == EOS for some 1 <= j' <= j, shift j reads EOS.
+ *   ids[t][h] = offsets[h] + floormod(int64(sum_{j<order(h)} s_j * m[h][j] mod 2^64), V_h)
+ * ids: device int32 [T][H].  Also writes batch->ngram_context_out when non-NULL
+ * (also when T == 0 and R > 0).  batch conv fields are ignored.
+ */
+int ple_ngram_ids(const ple_hash_desc* hash, const ple_batch_desc* batch, int32_t* ids, void* stream);
+
+/*
+ * Row gather ([P1] 关键源码片段, the embedding lookup; [P4] FP8 tables):
+ *   rows[t][h*D + c] = table[ids[t][h]][c]                         (bf16, bit copy)
+ *   rows[t][h*D + c] = bf16(float(e4m3fn(q[id][c])) * scale[id])   (fp8: one fp32
+ *                      multiply, round-to-nearest-even; NaN codes give 0x7FC0)
+ * ids: device int32 [T][H], every id in [0, num_rows) (ids outside are clamped
+ * into range, so a bad id never reads outside the table).  rows: device bf16
+ * [T][H*D].  table may be mapped pinned host memory (see ple_host_alloc).
+ */
+int ple_gather(const ple_table_desc* table, const int32_t* ids, int64_t num_tokens, int32_t num_heads,
+               uint16_t* rows, void* stream);
+
+/*
+ * Fused ids + gather in one kernel: the IDs stay on chip.  rows: device bf16
+ * [T][H*D] as in ple_gather; ids_out: device int32 [T][H] or NULL.  Also
+ * writes batch->ngram_context_out when non-NULL.
+ */
+int ple_lookup(const ple_hash_desc* hash, const ple_table_desc* table, const ple_batch_desc* batch,
+               int32_t* ids_out, uint16_t* rows, void* stream);
+
+/*
+ * Side-stream prefetch of one layer's rows ([P1] 关键源码片段 start_prefetch;
+ * [P2] 实现拆解 item 4, persistent staging buffer): ple_lookup with the
+ * layer's hash and table, into staging (device bf16 [T][H*D]).  Intended for
+ * a second stream; the caller orders the streams with events.  T == 0 returns
+ * at once.
+ */
+int ple_prefetch(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging, void* stream);
+
+/*
+ * Merged key/value projection ([P3] 实现拆解 item 1):
+ *   kv[t][o] = bf16(sum_i x[t][i] * w[o][i]), fp32 accumulation, no bias.
+ * x: device bf16 [T][K]; w: device bf16 [O][K]; kv: device bf16 [T][O].
+ * K a multiple of 64, O a multiple of 16.
+ */
+int ple_kv_proj(const uint16_t* x, const uint16_t* w, int64_t num_tokens, int32_t k_dim, int32_t out_dim,
+                uint16_t* kv, void* stream);
+
+/*
+ * Gate ([P3] 实现拆解 item 2, PLE gating and normalisation).  Per token, with
+ * h = hidden[t], k = kv[t][0:N], v = kv[t][N:2N]:
+ *   s = <h,k> / (sqrt(mean(h^2)+eps) * sqrt(mean(k^2)+eps) * sqrt(N)),
+ *   g = 1/(1+exp(-s)),  out[t][c] = bf16(g * v[c]),  gate[t] = g (fp32).
+ * hidden: device bf16 [T][N]; kv: device bf16 [T][2N]; out: device bf16 [T][N];
+ * gate: device fp32 [T] or NULL.  N a multiple of 8.
+ */
+int ple_gate(const uint16_t* hidden, const uint16_t* kv, int64_t num_tokens, int32_t n, float eps,
+             uint16_t* out, float* gate, void* stream);
+
+/*
+ * Dilated causal depthwise short convolution ([P3] 实现拆解 item 2):
+ *   y[t][c] = bf16(sum_{i<Kc} w[c][Kc-1-i] * x~(t - i*d, c)),
+ *   x~(p, c) = x[p][c] if p >= a (start of t's request), else
+ *              conv_state[r][S-(a-p)][c] if given, else 0.
+ * Uses batch->query_start_loc, num_tokens, num_reqs, conv_state and
+ * conv_state_out (the last S inputs of conv_state[r] ++ x[a:b], written also
+ * when T == 0 and R > 0).  x, y: device bf16 [T][N]; w: device bf16 [N][Kc].
+ * y must not alias x.  N a multiple of 8.
+ */
+int ple_conv(const uint16_t* x, const ple_batch_desc* batch, const uint16_t* w, int32_t n, int32_t kernel,
+             int32_t dilation, uint16_t* y, void* stream);
+
+/*
+ * Whole per-layer path in stream order: lookup (or the rows already staged by
+ * ple_prefetch when prefetched_rows != NULL) -> kv_proj -> gate -> conv.
+ * hidden: device bf16 [T][N]; out: device bf16 [T][N]; gate: device fp32 [T]
+ * or NULL; workspace: device memory of at least
+ * ple_prefill_workspace_bytes(layer, T) bytes, 256-byte aligned (holds rows,
+ * kv and the gated value between kernels; not read before being written).
+ */
+int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
+                      const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* workspace,
+                      size_t workspace_bytes, void* stream);
+size_t ple_prefill_workspace_bytes(const ple_layer_desc* layer, int64_t max_tokens);
+
+/*
+ * Pinned host memory the GPU reads directly ([P1] 功能与动机 and 关键源码片段,
+ * a table allocated page-locked and read through unified addressing).
+ * ple_host_alloc: page-locked, mapped, portable allocation of `bytes`;
+ * *host receives the host address and *device the address kernels use (the
+ * same value on this platform).  Synchronous.  ple_host_free releases it.
+ */
+int ple_host_alloc(size_t bytes, void** host, void** device);
+int ple_host_free(void* host);
+
+/*
+ * A stream restricted to the first num_cus compute units of the current
+ * device, for running the prefetch beside the main stream ([P2] 实现拆解
+ * item 4 launches the lookup on a side stream with half the grid).  Default
+ * priority.  ple_stream_destroy releases it.
+ */
+int ple_stream_create_cu_masked(int32_t num_cus, void** stream);
+int ple_stream_destroy(void* stream);
+
+/* Message for the last failure on the calling thread ("" if none). */
+const char* ple_error_message(void);
+/* Library version string. */
+const char* ple_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLE_H */

@@ -1,0 +1,271 @@
+"""MI355X-native per-layer n-gram embedding (PLE / Engram) lookup.
+
+Thin Python binding over libple (include/ple.h).  The functions keep the C
+names and only marshal torch tensors into the C descriptors: every step of the
+path runs in libple's HIP kernels on the tensors' device, on the current torch
+stream unless a stream is given.  PyTorch provides device memory and streams.
+
+    hp = HashParams(multipliers, vocab_sizes, offsets, heads_per_ngram=4, context_len=2, eos_token_id=0)
+    tb = Table.from_tensor(table)                 # bf16 [rows, D] or uint8 codes + fp32 scales
+    rows = ple_lookup(hp, tb, input_ids, query_start_loc)
+    kv = ple_kv_proj(rows, kv_weight)
+    out, g = ple_gate(hidden, kv)
+    y = ple_conv(out, query_start_loc, conv_weight, dilation=3)
+
+Errors raise RuntimeError with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import capi
+from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_ERR_DEVICE, PLE_ERR_INVALID_ARGUMENT,  # noqa: F401
+                   PLE_ERR_UNSUPPORTED, PLE_ERR_WORKSPACE, PLE_MAX_CONTEXT, PLE_MAX_HEADS, PLE_OK)
+
+__all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_lookup", "ple_prefetch",
+           "ple_kv_proj", "ple_gate", "ple_conv", "ple_prefill_fused", "ple_prefill_workspace_bytes",
+           "ple_host_alloc", "ple_host_free", "HostBuffer", "ple_stream_create_cu_masked", "ple_stream_destroy",
+           "ple_error_message", "ple_version", "library"]
+
+
+def library() -> ctypes.CDLL:
+    return capi.load()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class HashParams:
+    """One layer's hash constants (host memory, read during each call)."""
+
+    def __init__(self, multipliers, vocab_sizes, offsets, *, heads_per_ngram: int, context_len: int,
+                 eos_token_id: int, first_head: int = 0):
+        self.multipliers = np.ascontiguousarray(np.asarray(multipliers, dtype=np.int64))
+        self.vocab_sizes = np.ascontiguousarray(np.asarray(vocab_sizes, dtype=np.int64))
+        self.offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        self.heads_per_ngram = int(heads_per_ngram)
+        self.context_len = int(context_len)
+        self.eos_token_id = int(eos_token_id)
+        self.first_head = int(first_head)
+        self.num_heads = int(self.vocab_sizes.shape[0])
+
+    def desc(self) -> capi.ple_hash_desc:
+        return capi.ple_hash_desc(self.num_heads, self.heads_per_ngram, self.context_len, self.first_head,
+                                  self.eos_token_id, 0, self.multipliers.ctypes.data, self.vocab_sizes.ctypes.data,
+                                  self.offsets.ctypes.data)
+
+
+class Table:
+    """An embedding table: a device tensor, or the device address of mapped pinned host memory."""
+
+    def __init__(self, ptr: int, num_rows: int, dim: int, dtype: int, row_scales_ptr: int | None = None,
+                 keepalive=()):
+        self.ptr, self.num_rows, self.dim, self.dtype = int(ptr), int(num_rows), int(dim), int(dtype)
+        self.row_scales_ptr = row_scales_ptr
+        self._keepalive = keepalive
+
+    @classmethod
+    def from_tensor(cls, table: torch.Tensor, row_scales: torch.Tensor | None = None) -> "Table":
+        if table.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+            dt = PLE_DTYPE_BF16
+        elif table.dtype in (torch.uint8, torch.float8_e4m3fn):
+            dt = PLE_DTYPE_FP8_E4M3
+        else:
+            raise ValueError(f"unsupported table dtype {table.dtype}")
+        return cls(_ptr(table), table.shape[0], table.shape[1], dt, _ptr(row_scales), (table, row_scales))
+
+    def desc(self) -> capi.ple_table_desc:
+        return capi.ple_table_desc(self.ptr, self.num_rows, self.dim, self.dtype, self.row_scales_ptr)
+
+
+class Layer:
+    """A layer's hash, table, projection, gate and conv parameters."""
+
+    def __init__(self, hash: HashParams, table: Table, kv_weight: torch.Tensor, conv_weight: torch.Tensor, *,
+                 conv_dilation: int, eps: float = 1e-6):
+        self.hash, self.table = hash, table
+        self.kv_weight, self.conv_weight = kv_weight, conv_weight
+        self.hidden = int(conv_weight.shape[0])
+        self.conv_kernel = int(conv_weight.shape[1])
+        self.conv_dilation = int(conv_dilation)
+        self.eps = float(eps)
+
+    def desc(self) -> capi.ple_layer_desc:
+        return capi.ple_layer_desc(self.hash.desc(), self.table.desc(), _ptr(self.kv_weight), self.hidden,
+                                   self.eps, _ptr(self.conv_weight), self.conv_kernel, self.conv_dilation)
+
+
+def _batch(input_ids, query_start_loc, ngram_context=None, ngram_context_out=None, conv_state=None,
+           conv_state_out=None, num_tokens=None) -> capi.ple_batch_desc:
+    T = int(input_ids.shape[0]) if input_ids is not None else int(num_tokens)
+    R = int(query_start_loc.shape[0]) - 1
+    return capi.ple_batch_desc(_ptr(input_ids), _ptr(query_start_loc), T, R, 0, _ptr(ngram_context),
+                               _ptr(ngram_context_out), _ptr(conv_state), _ptr(conv_state_out))
+
+
+def _device_of(t: torch.Tensor) -> torch.device:
+    return t.device
+
+
+def ple_ngram_ids(hash: HashParams, input_ids, query_start_loc, *, ngram_context=None, ngram_context_out=None,
+                  ids=None, stream=None):
+    T = input_ids.shape[0]
+    if ids is None:
+        ids = torch.empty((T, hash.num_heads), dtype=torch.int32, device=input_ids.device)
+    h = hash.desc()
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    capi.check(capi.load().ple_ngram_ids(ctypes.byref(h), ctypes.byref(b), _ptr(ids), _stream(stream)),
+               "ple_ngram_ids")
+    return ids
+
+
+def ple_gather(table: Table, ids, *, rows=None, stream=None):
+    T, H = ids.shape
+    if rows is None:
+        rows = torch.empty((T, H * table.dim), dtype=torch.bfloat16, device=ids.device)
+    t = table.desc()
+    capi.check(capi.load().ple_gather(ctypes.byref(t), _ptr(ids), T, H, _ptr(rows), _stream(stream)), "ple_gather")
+    return rows
+
+
+def ple_lookup(hash: HashParams, table: Table, input_ids, query_start_loc, *, ngram_context=None,
+               ngram_context_out=None, ids_out=None, rows=None, stream=None):
+    T = input_ids.shape[0]
+    if rows is None:
+        rows = torch.empty((T, hash.num_heads * table.dim), dtype=torch.bfloat16, device=input_ids.device)
+    h, t = hash.desc(), table.desc()
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    capi.check(capi.load().ple_lookup(ctypes.byref(h), ctypes.byref(t), ctypes.byref(b), _ptr(ids_out), _ptr(rows),
+                                      _stream(stream)), "ple_lookup")
+    return rows
+
+
+def ple_prefetch(layer: Layer, input_ids, query_start_loc, staging, *, ngram_context=None, ngram_context_out=None,
+                 stream=None):
+    L = layer.desc()
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    capi.check(capi.load().ple_prefetch(ctypes.byref(L), ctypes.byref(b), _ptr(staging), _stream(stream)),
+               "ple_prefetch")
+    return staging
+
+
+def ple_kv_proj(x, w, *, kv=None, stream=None):
+    T, K = x.shape
+    O = w.shape[0]
+    if kv is None:
+        kv = torch.empty((T, O), dtype=torch.bfloat16, device=x.device)
+    capi.check(capi.load().ple_kv_proj(_ptr(x), _ptr(w), T, K, O, _ptr(kv), _stream(stream)), "ple_kv_proj")
+    return kv
+
+
+def ple_gate(hidden, kv, *, eps: float = 1e-6, out=None, gate=None, want_gate: bool = True, stream=None):
+    T, N = hidden.shape
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=hidden.device)
+    if gate is None and want_gate:
+        gate = torch.empty((T,), dtype=torch.float32, device=hidden.device)
+    capi.check(capi.load().ple_gate(_ptr(hidden), _ptr(kv), T, N, eps, _ptr(out), _ptr(gate), _stream(stream)),
+               "ple_gate")
+    return out, gate
+
+
+def ple_conv(x, query_start_loc, w, *, dilation: int, conv_state=None, conv_state_out=None, y=None, stream=None):
+    T, N = x.shape
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    b = _batch(None, query_start_loc, conv_state=conv_state, conv_state_out=conv_state_out, num_tokens=T)
+    capi.check(capi.load().ple_conv(_ptr(x), ctypes.byref(b), _ptr(w), N, w.shape[1], dilation, _ptr(y),
+                                    _stream(stream)), "ple_conv")
+    return y
+
+
+def ple_prefill_workspace_bytes(layer: Layer, max_tokens: int) -> int:
+    L = layer.desc()
+    return int(capi.load().ple_prefill_workspace_bytes(ctypes.byref(L), int(max_tokens)))
+
+
+def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefetched_rows=None, ngram_context=None,
+                      ngram_context_out=None, conv_state=None, conv_state_out=None, out=None, gate=None,
+                      workspace=None, stream=None):
+    T, N = hidden.shape
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=hidden.device)
+    need = ple_prefill_workspace_bytes(layer, T)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=hidden.device)
+    L = layer.desc()
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out)
+    capi.check(capi.load().ple_prefill_fused(ctypes.byref(L), ctypes.byref(b), _ptr(hidden), _ptr(prefetched_rows),
+                                             _ptr(out), _ptr(gate), _ptr(workspace), workspace.numel(),
+                                             _stream(stream)), "ple_prefill_fused")
+    return out
+
+
+class HostBuffer:
+    """Mapped pinned host memory from ple_host_alloc (freed by close() or at collection)."""
+
+    def __init__(self, nbytes: int):
+        h, d = ctypes.c_void_p(), ctypes.c_void_p()
+        capi.check(capi.load().ple_host_alloc(int(nbytes), ctypes.byref(h), ctypes.byref(d)), "ple_host_alloc")
+        self.host, self.device, self.nbytes = h.value, d.value, int(nbytes)
+
+    def numpy(self, dtype, shape) -> np.ndarray:
+        """A numpy view of the host side (valid while this object lives)."""
+        buf = (ctypes.c_char * self.nbytes).from_address(self.host)
+        return np.frombuffer(buf, dtype=dtype, count=int(np.prod(shape))).reshape(shape)
+
+    def close(self):
+        if self.host:
+            capi.check(capi.load().ple_host_free(self.host), "ple_host_free")
+            self.host = self.device = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ple_host_alloc(nbytes: int) -> HostBuffer:
+    return HostBuffer(nbytes)
+
+
+def ple_host_free(buf: HostBuffer) -> None:
+    buf.close()
+
+
+def ple_stream_create_cu_masked(num_cus: int) -> torch.cuda.ExternalStream:
+    s = ctypes.c_void_p()
+    capi.check(capi.load().ple_stream_create_cu_masked(int(num_cus), ctypes.byref(s)), "ple_stream_create_cu_masked")
+    return torch.cuda.ExternalStream(s.value)
+
+
+def ple_stream_destroy(stream) -> None:
+    capi.check(capi.load().ple_stream_destroy(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream),
+               "ple_stream_destroy")
+
+
+def ple_error_message() -> str:
+    return capi.error_message()
+
+
+def ple_version() -> str:
+    return capi.load().ple_version().decode()

@@ -1,0 +1,87 @@
+// Device-side helpers shared by the libple kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ple.h"
+
+namespace ple {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Per-call hash constants, passed by value as a kernel argument so that calls
+// on different streams (a prefetch for the next layer beside the current one)
+// never share mutable state.
+struct HashParams {
+    uint64_t mult[PLE_MAX_HEADS][PLE_MAX_CONTEXT + 1];
+    uint64_t barrett[PLE_MAX_HEADS];   // floor((2^64 - 1) / V_h)
+    uint32_t vocab[PLE_MAX_HEADS];     // V_h < 2^31
+    uint32_t wrap_mod[PLE_MAX_HEADS];  // 2^64 mod V_h
+    uint32_t offset[PLE_MAX_HEADS];    // offsets[h]
+    uint8_t order[PLE_MAX_HEADS];      // n-gram order of head h (2..C+1)
+    int32_t num_heads;
+    int32_t context_len;
+    int32_t eos;
+    int32_t pad;
+};
+
+// bf16 <-> fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// Same, with any NaN mapped to the canonical quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t pack_bf16x2_canon(float lo, float hi) {
+    uint32_t w = pack_bf16x2(lo, hi);
+    if (lo != lo) w = (w & 0xFFFF0000u) | 0x7FC0u;
+    if (hi != hi) w = (w & 0x0000FFFFu) | 0x7FC00000u;
+    return w;
+}
+
+// Largest r in [0, R-1] with qsl[r] <= t (the request owning token t for a
+// valid qsl; an in-range index for any qsl).  R >= 1.
+__device__ __forceinline__ int find_request(const int32_t* __restrict__ qsl, int R, int64_t t) {
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)qsl[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// floor((x * m) / 2^64) for 64-bit unsigned x, m.
+__device__ __forceinline__ uint64_t mulhi64(uint64_t x, uint64_t m) { return __umul64hi(x, m); }
+
+// Signed floor modulo of the wrapped 64-bit sum `acc` (read as int64) by V:
+//   acc <  2^63:  acc mod V
+//   acc >= 2^63:  (acc - 2^64) mod V = (acc mod V - 2^64 mod V) mod V
+// acc mod V by Barrett reduction with b = floor((2^64-1)/V): the quotient
+// estimate is short by at most 2, so two conditional subtractions finish it.
+__device__ __forceinline__ uint32_t floor_mod_wrapped(uint64_t acc, uint32_t V, uint64_t b, uint32_t wrap) {
+    uint64_t q = mulhi64(acc, b);
+    uint64_t r = acc - q * (uint64_t)V;
+    if (r >= V) r -= V;
+    if (r >= V) r -= V;
+    uint32_t rr = (uint32_t)r;
+    if ((int64_t)acc < 0) rr = rr >= wrap ? rr - wrap : rr + (V - wrap);
+    return rr;
+}
+
+}  // namespace ple

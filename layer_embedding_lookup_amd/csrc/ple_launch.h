@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (ple_api.cpp) and the kernels.
+#pragma once
+
+#include "ple_device.h"
+
+namespace ple {
+
+enum { kModeHash = 0, kModeIds = 1 };
+
+struct LookupArgs {
+    const int32_t* tok;
+    const int32_t* qsl;
+    const int32_t* ctx;
+    const int32_t* ids_in;
+    int32_t* ids_out;
+    const void* table;
+    const float* scales;
+    uint16_t* rows;
+    int64_t num_tokens;
+    int64_t num_rows;
+    int32_t num_reqs;
+    int32_t num_heads;
+    int32_t dim;
+    int32_t tokens_per_block;
+    int32_t cpr_log2;  // log2(16-byte input chunks per row), or -1
+    int32_t pad;
+};
+
+hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int32_t* qsl, int64_t T, int R,
+                            const int32_t* ctx, int32_t* ids, hipStream_t s);
+hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T, int R, int C, int32_t eos,
+                              const int32_t* ctx, int32_t* ctx_out, hipStream_t s);
+int lookup_tokens_per_block(int64_t T, int H);
+hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s);
+
+hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
+                          hipStream_t s);
+
+hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, uint16_t* out,
+                       float* gate, hipStream_t s);
+hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
+                       const uint16_t* w, int N, int K, int d, uint16_t* y, hipStream_t s);
+hipError_t launch_conv_state_out(const uint16_t* x, const int32_t* qsl, int64_t T, int R,
+                                 const uint16_t* state, int N, int S, uint16_t* state_out, hipStream_t s);
+
+}  // namespace ple

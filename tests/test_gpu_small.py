@@ -1,0 +1,470 @@
+"""GPU parity of every libple entry point against the oracle, at sizes the
+oracle finishes in seconds (several tiles plus ragged tails) and on the edge
+cases of the method.  IDs, rows and fp8 dequant: bit-exact.  kv_proj: within
+one bf16 ulp.  Gate and conv bf16 outputs: max-abs 2e-2 (and at most one bf16
+ulp in practice); the fp32 gate value: rel 1e-5."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import layer_embedding_lookup_amd as ple
+import oracle
+import workloads as wl
+from gpu_util import (DEV, bf16_f64, bf16_ulp_distance, dev, dev_bf16, hash_params, host_bits, log,
+                      oracle_ids)
+
+pytestmark = pytest.mark.gpu
+
+GATE_ABS_TOL = 2e-2
+CONV_ABS_TOL = 2e-2
+GATE_REL_TOL = 1e-5
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    log(f"device: {torch.cuda.get_device_name(0)}; {ple.ple_version()}")
+
+
+# ------------------------------------------------------------------ ids
+
+@pytest.mark.parametrize("cfg_idx", [1, 2, 3, 4, 5])
+def test_ids_parity_configs(cfg_idx):
+    cfg = wl.CONFIGS[cfg_idx]
+    b = wl.make_batch(cfg, layers=2)
+    for layer in range(2):
+        log(f"ids cfg{cfg_idx} layer{layer} T={cfg.T} R={b.R} H={cfg.H}")
+        want, want_ctx = oracle_ids(b, layer, want_context_out=True)
+        ctx_d = dev(b.ngram_context) if b.ngram_context is not None else None
+        ctx_out = torch.full((b.R, cfg.context_len), -1, dtype=torch.int32, device=DEV)
+        got = ple.ple_ngram_ids(hash_params(b, layer), dev(b.input_ids), dev(b.qsl), ngram_context=ctx_d,
+                                ngram_context_out=ctx_out)
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
+        np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
+
+
+def test_ids_cfg1_with_context():
+    b = wl.make_batch(wl.CONFIGS[1], with_context=True)
+    want = oracle_ids(b)
+    got = ple.ple_ngram_ids(hash_params(b), dev(b.input_ids), dev(b.qsl), ngram_context=dev(b.ngram_context))
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def _random_case(rng):
+    C = int(rng.integers(1, 8))
+    hpn = int(rng.integers(1, 5))
+    Hfull = min(C * hpn, 32)
+    first = int(rng.integers(0, Hfull))
+    H = int(rng.integers(1, min(Hfull - first, 32) + 1))
+    R = int(rng.integers(1, 40))
+    lens = rng.integers(0, 30, size=R)
+    lens[rng.random(R) < 0.2] = 0
+    qsl = wl.qsl_from_lengths(lens)
+    T = int(qsl[-1])
+    eos = int(rng.integers(0, 3))
+    toks = rng.integers(0, 12, size=T).astype(np.int32)  # EOS frequent
+    big = rng.random(T) < 0.4
+    toks[big] = rng.integers(0, 2 ** 31 - 1, size=int(big.sum()))
+    mult = rng.integers(-(1 << 63), (1 << 63) - 1, size=(H, C + 1), dtype=np.int64)
+    V = rng.integers(1, 2 ** 31 // 40, size=H).astype(np.int64)
+    V[rng.random(H) < 0.2] = 1
+    off = np.concatenate([[0], np.cumsum(V)[:-1]]).astype(np.int64)
+    ctx = rng.integers(0, 12, size=(R, C)).astype(np.int32) if rng.random() < 0.5 else None
+    return dict(C=C, hpn=hpn, first=first, H=H, qsl=qsl, toks=toks, eos=eos, mult=mult, V=V, off=off, ctx=ctx)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_ids_edge_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    c = _random_case(rng)
+    R = len(c["qsl"]) - 1
+    log(f"ids edge seed={seed} T={len(c['toks'])} R={R} C={c['C']} H={c['H']} first={c['first']}")
+    want, want_ctx = oracle.ngram_ids(c["toks"], c["qsl"], c["mult"], c["V"], c["off"], context_len=c["C"],
+                                      heads_per_ngram=c["hpn"], eos_token_id=c["eos"], ngram_context=c["ctx"],
+                                      first_head=c["first"], want_context_out=True)
+    hp = ple.HashParams(c["mult"], c["V"], c["off"], heads_per_ngram=c["hpn"], context_len=c["C"],
+                        eos_token_id=c["eos"], first_head=c["first"])
+    ctx_out = torch.full((R, c["C"]), -7, dtype=torch.int32, device=DEV)
+    toks = dev(c["toks"]) if len(c["toks"]) else torch.zeros(0, dtype=torch.int32, device=DEV)
+    got = ple.ple_ngram_ids(hp, toks, dev(c["qsl"]), ngram_context=None if c["ctx"] is None else dev(c["ctx"]),
+                            ngram_context_out=ctx_out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+    np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
+
+
+def test_ids_golden_cases():
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hash_cases.json")))["cases"]
+    for c in cases:
+        log(f"golden {c['name']}")
+        hp = ple.HashParams(np.asarray(c["multipliers"], np.int64), c["vocab_sizes"], c["offsets"],
+                            heads_per_ngram=c["heads_per_ngram"], context_len=c["context_len"],
+                            eos_token_id=c["eos"], first_head=c["first_head"])
+        ctx = None if c["context"] is None else dev(np.asarray(c["context"], np.int32))
+        ctx_out = torch.empty((len(c["qsl"]) - 1, c["context_len"]), dtype=torch.int32, device=DEV)
+        got = ple.ple_ngram_ids(hp, dev(np.asarray(c["input_ids"], np.int32)), dev(np.asarray(c["qsl"], np.int32)),
+                                ngram_context=ctx, ngram_context_out=ctx_out)
+        assert got.cpu().tolist() == c["expected_ids"], c["name"]
+        assert ctx_out.cpu().tolist() == c["expected_context_out"], c["name"]
+
+
+def test_ids_empty_batch_carries_context():
+    hp = ple.HashParams(np.ones((2, 3), np.int64), [11, 13], [0, 11], heads_per_ngram=1, context_len=2,
+                        eos_token_id=0)
+    ctx = dev(np.asarray([[4, 5], [6, 7], [8, 9]], np.int32))
+    ctx_out = torch.zeros((3, 2), dtype=torch.int32, device=DEV)
+    got = ple.ple_ngram_ids(hp, torch.zeros(0, dtype=torch.int32, device=DEV), dev(np.zeros(4, np.int32)),
+                            ngram_context=ctx, ngram_context_out=ctx_out)
+    assert got.shape == (0, 2)
+    assert ctx_out.cpu().tolist() == [[4, 5], [6, 7], [8, 9]]
+
+
+def test_ids_context_null_equals_all_eos():
+    b = wl.make_batch(wl.CONFIGS[2])
+    hp = hash_params(b)
+    a = ple.ple_ngram_ids(hp, dev(b.input_ids), dev(b.qsl))
+    z = ple.ple_ngram_ids(hp, dev(b.input_ids), dev(b.qsl),
+                          ngram_context=torch.zeros((b.R, 2), dtype=torch.int32, device=DEV))
+    assert torch.equal(a, z)
+
+
+def test_ids_chunked_equals_whole_on_gpu():
+    cfg = wl.CONFIGS[3]
+    b = wl.make_batch(cfg)
+    hp = hash_params(b)
+    qsl = b.qsl
+    r = int(np.argmax(np.diff(qsl)))  # the longest request
+    a0, a1 = int(qsl[r]), int(qsl[r + 1])
+    toks = b.input_ids[a0:a1]
+    whole = ple.ple_ngram_ids(hp, dev(toks), dev(np.asarray([0, len(toks)], np.int32)))
+    ctx = None
+    parts = []
+    cuts = sorted({0, 1, 5, len(toks) // 3, len(toks) // 3 + 1, len(toks) - 1, len(toks)})
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        out_ctx = torch.empty((1, 2), dtype=torch.int32, device=DEV)
+        parts.append(ple.ple_ngram_ids(hp, dev(toks[lo:hi]), dev(np.asarray([0, hi - lo], np.int32)),
+                                       ngram_context=ctx, ngram_context_out=out_ctx))
+        ctx = out_ctx
+    assert torch.equal(torch.cat(parts), whole)
+
+
+# ------------------------------------------------------------------ lookup / gather
+
+def _table_dev(cfg, seed=None):
+    q, sc = wl.make_table(cfg, seed=seed)
+    if cfg.table_dtype == "bf16":
+        t = dev_bf16(q)
+        return q, sc, ple.Table.from_tensor(t), (t,)
+    qt, st = dev(q), dev(sc)
+    return q, sc, ple.Table.from_tensor(qt, st), (qt, st)
+
+
+@pytest.mark.parametrize("cfg_idx", [1, 2])
+def test_lookup_parity_small_configs(cfg_idx):
+    cfg = wl.CONFIGS[cfg_idx]
+    b = wl.make_batch(cfg, layers=2)
+    table, _, tb, keep = _table_dev(cfg)
+    for layer in range(2):
+        log(f"lookup cfg{cfg_idx} layer{layer}")
+        ids = oracle_ids(b, layer)
+        want = oracle.gather_bf16(table, ids).reshape(cfg.T, -1)
+        ids_out = torch.empty((cfg.T, cfg.H), dtype=torch.int32, device=DEV)
+        ctx = dev(b.ngram_context) if b.ngram_context is not None else None
+        rows = ple.ple_lookup(hash_params(b, layer), tb, dev(b.input_ids), dev(b.qsl), ngram_context=ctx,
+                              ids_out=ids_out)
+        np.testing.assert_array_equal(ids_out.cpu().numpy(), ids)
+        np.testing.assert_array_equal(host_bits(rows), want)
+        rows2 = ple.ple_gather(tb, dev(ids))
+        np.testing.assert_array_equal(host_bits(rows2), want)
+
+
+def _small_fp8_cfg():
+    base = wl.CONFIGS[4]
+    import dataclasses
+    return dataclasses.replace(base, idx=40, T=700, vocab_base=5003)
+
+
+def test_lookup_fp8_small():
+    cfg = _small_fp8_cfg()
+    b = wl.make_batch(cfg)
+    q, sc, tb, keep = _table_dev(cfg)
+    ids = oracle_ids(b)
+    want = oracle.gather_fp8(q, sc, ids).reshape(cfg.T, -1)
+    rows = ple.ple_lookup(hash_params(b), tb, dev(b.input_ids), dev(b.qsl))
+    np.testing.assert_array_equal(host_bits(rows), want)
+
+
+def test_fp8_every_code_and_scale():
+    rng = np.random.default_rng(8)
+    D, nrows = 256, 64
+    codes = np.stack([rng.permutation(256) for _ in range(nrows)]).astype(np.uint8)
+    scales = np.exp(rng.uniform(-40, 40, nrows)).astype(np.float32)
+    scales[:4] = [1.0, 2.0 ** -20, 3.0e30, 1e-38]
+    ids = rng.integers(0, nrows, size=(50, 3)).astype(np.int32)
+    want = oracle.gather_fp8(codes, scales, ids).reshape(50, -1)
+    tb = ple.Table.from_tensor(dev(codes), dev(scales))
+    rows = ple.ple_gather(tb, dev(ids))
+    np.testing.assert_array_equal(host_bits(rows), want)
+
+
+@pytest.mark.parametrize("D", [32, 256, 512, 40])
+def test_gather_bf16_dims_and_clamping(D):
+    rng = np.random.default_rng(D)
+    nrows = 3000
+    table = rng.integers(0, 65536, size=(nrows, D), dtype=np.uint16)
+    ids = rng.integers(0, nrows, size=(333, 5)).astype(np.int32)
+    ids[0, 0], ids[1, 1], ids[2, 2] = -5, nrows, 2 ** 31 - 1   # clamped into [0, rows)
+    clamped = np.clip(ids, 0, nrows - 1)
+    tb = ple.Table.from_tensor(dev_bf16(table))
+    rows = ple.ple_gather(tb, dev(ids))
+    np.testing.assert_array_equal(host_bits(rows), table[clamped.reshape(-1)].reshape(333, -1))
+
+
+def test_lookup_head_subset_matches_full():
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    table, _, tb, keep = _table_dev(cfg)
+    full = ple.ple_lookup(hash_params(b), tb, dev(b.input_ids), dev(b.qsl), ngram_context=dev(b.ngram_context))
+    D = cfg.D
+    for first, H in [(0, 4), (4, 4), (3, 2), (7, 1)]:
+        part = ple.ple_lookup(hash_params(b, first_head=first, num_heads=H), tb, dev(b.input_ids), dev(b.qsl),
+                              ngram_context=dev(b.ngram_context))
+        assert torch.equal(part, full.view(cfg.T, cfg.H, D)[:, first:first + H].reshape(cfg.T, -1))
+
+
+# ------------------------------------------------------------------ kv_proj
+
+@pytest.mark.parametrize("M,K,O", [(24, 128, 256), (1, 64, 16), (300, 192, 80), (129, 128, 144),
+                                   (256, 2048, 4096), (1000, 512, 1024)])
+def test_kv_proj_parity(M, K, O):
+    log(f"kv_proj M={M} K={K} O={O}")
+    x = wl.normal_bf16((M, K), 100 + M, 0.02)
+    w = wl.normal_bf16((O, K), 200 + O, 12.5 / np.sqrt(K))
+    want = oracle.kv_proj(x, w)
+    got = host_bits(ple.ple_kv_proj(dev_bf16(x), dev_bf16(w)))
+    d = bf16_ulp_distance(got, want)
+    assert d.max() <= 1, d.max()
+    assert (d > 0).mean() < 0.01
+
+
+def test_kv_proj_sampled_rows_at_prefill_shape():
+    cfg = wl.CONFIGS[3]
+    M, K, O = cfg.T, cfg.H * cfg.D, 2 * cfg.N
+    x = wl.normal_bf16((M, K), 5, 0.02)
+    w = wl.make_kv_weight(cfg)
+    got = host_bits(ple.ple_kv_proj(dev_bf16(x), dev_bf16(w)))
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(M - 64, M),
+                                     np.random.default_rng(0).integers(0, M, 64)]))
+    want = oracle.kv_proj(x[rows], w)
+    d = bf16_ulp_distance(got[rows], want)
+    assert d.max() <= 1 and (d > 0).mean() < 0.01
+
+
+# ------------------------------------------------------------------ gate
+
+@pytest.mark.parametrize("T,N", [(24, 128), (256, 2048), (333, 4096), (5, 8), (7, 4104)])
+def test_gate_parity(T, N):
+    log(f"gate T={T} N={N}")
+    h = wl.normal_bf16((T, N), 300 + N, 1.0)
+    kv = wl.normal_bf16((T, 2 * N), 400 + N, 0.25)
+    want, g_want = oracle.gate(h, kv, 1e-6)
+    out, g = ple.ple_gate(dev_bf16(h), dev_bf16(kv), eps=1e-6)
+    got = host_bits(out)
+    assert np.abs(bf16_f64(got) - bf16_f64(want)).max() <= GATE_ABS_TOL
+    assert bf16_ulp_distance(got, want).max() <= 1
+    gg = g.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(gg, g_want, rtol=GATE_REL_TOL, atol=0)
+    assert ((gg > 0) & (gg < 1)).all()
+
+
+def test_gate_closed_forms_on_gpu():
+    N = 256
+    h = np.zeros((2, N))
+    h[:, ::2] = 1.0
+    k = np.zeros((2, N))
+    k[:, 1::2] = -0.75
+    v = np.linspace(-1, 1, N)[None].repeat(2, 0)
+    bits = lambda a: np.asarray([oracle.bf16_from_double(float(x)) for x in a.ravel()], np.uint16).reshape(a.shape)
+    out, g = ple.ple_gate(dev_bf16(bits(h)), dev_bf16(np.concatenate([bits(k), bits(v)], 1)))
+    assert (g.cpu().numpy() == 0.5).all()
+    np.testing.assert_array_equal(bf16_f64(host_bits(out)), bf16_f64(bits(v)) / 2)
+
+
+# ------------------------------------------------------------------ conv
+
+CONV_CASES = [
+    # (lengths, N, K, d, with_state)
+    ([7, 1, 13, 3], 128, 4, 2, False),
+    ([7, 1, 13, 3], 128, 4, 2, True),
+    ([1] * 64, 2048, 4, 3, True),
+    ([0, 5, 0, 0, 40, 1, 0], 64, 3, 5, True),
+    ([50, 20], 64, 1, 1, False),
+    ([33, 0, 9], 72, 7, 2, True),   # generic kernel size path
+    ([100], 16, 2, 9, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CONV_CASES)))
+def test_conv_parity(case):
+    lens, N, K, d, with_state = CONV_CASES[case]
+    log(f"conv case {case}: R={len(lens)} N={N} K={K} d={d} state={with_state}")
+    qsl = wl.qsl_from_lengths(lens)
+    T, R, S = int(qsl[-1]), len(lens), (K - 1) * d
+    x = wl.normal_bf16((T, N), 500 + case, 0.5)
+    w = wl.uniform_bf16((N, K), 600 + case, -0.5, 0.5)
+    st = wl.normal_bf16((R, S, N), 700 + case, 0.125) if with_state and S > 0 else None
+    want, st_want = oracle.conv(x, qsl, w, d, state=st, want_state_out=True)
+    st_out = torch.empty((R, S, N), dtype=torch.bfloat16, device=DEV) if S > 0 else None
+    xd = dev_bf16(x) if T else torch.zeros((0, N), dtype=torch.bfloat16, device=DEV)
+    y = ple.ple_conv(xd, dev(qsl), dev_bf16(w), dilation=d, conv_state=None if st is None else dev_bf16(st),
+                     conv_state_out=st_out)
+    got = host_bits(y)
+    assert np.abs(bf16_f64(got) - bf16_f64(want)).max() <= CONV_ABS_TOL
+    assert bf16_ulp_distance(got, want).max() <= 1
+    if S > 0:
+        np.testing.assert_array_equal(host_bits(st_out), st_want)
+
+
+def test_conv_chunked_equals_whole_on_gpu():
+    N, K, d = 256, 4, 3
+    x = wl.normal_bf16((200, N), 801, 0.5)
+    w = wl.uniform_bf16((N, K), 802, -0.5, 0.5)
+    S = (K - 1) * d
+    whole = ple.ple_conv(dev_bf16(x), dev(np.asarray([0, 200], np.int32)), dev_bf16(w), dilation=d)
+    st = None
+    parts = []
+    for lo, hi in [(0, 3), (3, 4), (4, 120), (120, 121), (121, 200)]:
+        so = torch.empty((1, S, N), dtype=torch.bfloat16, device=DEV)
+        parts.append(ple.ple_conv(dev_bf16(x[lo:hi]), dev(np.asarray([0, hi - lo], np.int32)), dev_bf16(w),
+                                  dilation=d, conv_state=st, conv_state_out=so))
+        st = so
+    assert torch.equal(torch.cat(parts), whole)
+
+
+# ------------------------------------------------------------------ fused prefill
+
+def _layer(cfg, b, layer=0):
+    table, scales, tb, keep = _table_dev(cfg)
+    kvw = wl.make_kv_weight(cfg, layer=layer)
+    cw = wl.make_conv_weight(cfg)
+    L = ple.Layer(hash_params(b, layer), tb, dev_bf16(kvw), dev_bf16(cw), conv_dilation=cfg.conv_dilation,
+                  eps=cfg.eps)
+    return L, table, scales, kvw, cw, keep
+
+
+def _oracle_chain(cfg, b, table, scales, kvw, cw, hidden, tokens=None, layer=0):
+    args = dict(input_ids=b.input_ids, qsl=b.qsl, multipliers=b.multipliers[layer], vocab_sizes=b.vocab_sizes,
+                offsets=b.offsets, context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram,
+                eos_token_id=wl.EOS, ngram_context=b.ngram_context)
+    return oracle.prefill(args, table, scales, hidden, kvw, cw, cfg.conv_dilation, qsl=b.qsl, eps=cfg.eps,
+                          conv_state=b.conv_state, tokens=tokens)
+
+
+@pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2"])
+def test_prefill_fused_parity_small(variant):
+    cfg = wl.CONFIGS[2 if variant == "cfg2" else 1]
+    if variant == "cfg1-ctx-state":
+        b = wl.make_batch(cfg, with_context=True, with_state=True)
+    else:
+        b = wl.make_batch(cfg)
+    log(f"prefill {variant}")
+    L, table, scales, kvw, cw, keep = _layer(cfg, b)
+    hidden = wl.make_hidden(cfg)
+    ref = _oracle_chain(cfg, b, table, scales, kvw, cw, hidden)
+    S = cfg.S
+    st_out = torch.empty((b.R, S, cfg.N), dtype=torch.bfloat16, device=DEV)
+    ctx_out = torch.empty((b.R, cfg.context_len), dtype=torch.int32, device=DEV)
+    gate = torch.empty((cfg.T,), dtype=torch.float32, device=DEV)
+    out = ple.ple_prefill_fused(L, dev(b.input_ids), dev(b.qsl), dev_bf16(hidden),
+                                ngram_context=None if b.ngram_context is None else dev(b.ngram_context),
+                                ngram_context_out=ctx_out,
+                                conv_state=None if b.conv_state is None else dev_bf16(b.conv_state),
+                                conv_state_out=st_out, gate=gate)
+    got = host_bits(out)
+    assert np.abs(bf16_f64(got) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
+    # the gate sees kv rounded to bf16 on both sides, which may differ by one ulp: compare loosely
+    np.testing.assert_allclose(gate.cpu().numpy(), ref["gate"], rtol=5e-3)
+    _, want_ctx = oracle_ids(b, want_context_out=True)
+    np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
+    _, st_ref = oracle.conv(ref["gated"], b.qsl, cw, cfg.conv_dilation, state=b.conv_state, want_state_out=True)
+    d = bf16_ulp_distance(host_bits(st_out), st_ref)
+    assert d.max() <= 1
+
+
+def test_prefill_with_prefetched_rows_equals_plain():
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    L, table, scales, kvw, cw, keep = _layer(cfg, b)
+    hidden = dev_bf16(wl.make_hidden(cfg))
+    toks, qsl, ctx = dev(b.input_ids), dev(b.qsl), dev(b.ngram_context)
+    plain = ple.ple_prefill_fused(L, toks, qsl, hidden, ngram_context=ctx)
+    side = torch.cuda.Stream()
+    staging = torch.empty((cfg.T, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+    ev0 = torch.cuda.Event()
+    ev0.record()
+    side.wait_event(ev0)
+    ple.ple_prefetch(L, toks, qsl, staging, ngram_context=ctx, stream=side)
+    ev = torch.cuda.Event()
+    ev.record(side)
+    torch.cuda.current_stream().wait_event(ev)
+    pre = ple.ple_prefill_fused(L, toks, qsl, hidden, prefetched_rows=staging, ngram_context=ctx)
+    assert torch.equal(plain, pre)
+
+
+def test_prefill_empty_batch():
+    cfg = wl.CONFIGS[1]
+    b = wl.make_batch(cfg)
+    L, *_ = _layer(cfg, b)
+    out = ple.ple_prefill_fused(L, torch.zeros(0, dtype=torch.int32, device=DEV),
+                                torch.zeros(1, dtype=torch.int32, device=DEV),
+                                torch.zeros((0, cfg.N), dtype=torch.bfloat16, device=DEV),
+                                workspace=torch.empty(256, dtype=torch.uint8, device=DEV))
+    assert out.shape == (0, cfg.N)
+
+
+def test_repeat_runs_bit_identical():
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    L, *_ = _layer(cfg, b)
+    hidden = dev_bf16(wl.make_hidden(cfg))
+    a = ple.ple_prefill_fused(L, dev(b.input_ids), dev(b.qsl), hidden, ngram_context=dev(b.ngram_context))
+    c = ple.ple_prefill_fused(L, dev(b.input_ids), dev(b.qsl), hidden, ngram_context=dev(b.ngram_context))
+    assert torch.equal(a, c)
+
+
+def test_host_mapped_table_matches_hbm():
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    table, _ = wl.make_table(cfg)
+    hb = ple.ple_host_alloc(table.nbytes)
+    hv = hb.numpy(np.uint16, table.shape)
+    hv[...] = table
+    tb_host = ple.Table(hb.device, cfg.num_rows, cfg.D, ple.PLE_DTYPE_BF16)
+    tb_dev = ple.Table.from_tensor(dev_bf16(table))
+    hp = hash_params(b)
+    r_host = ple.ple_lookup(hp, tb_host, dev(b.input_ids), dev(b.qsl), ngram_context=dev(b.ngram_context))
+    r_dev = ple.ple_lookup(hp, tb_dev, dev(b.input_ids), dev(b.qsl), ngram_context=dev(b.ngram_context))
+    torch.cuda.synchronize()
+    assert torch.equal(r_host, r_dev)
+    hb.close()
+
+
+def test_cu_masked_stream_prefetch():
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    L, *_ = _layer(cfg, b)
+    s = ple.ple_stream_create_cu_masked(64)
+    try:
+        staging = torch.empty((cfg.T, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+        ev0 = torch.cuda.Event()
+        ev0.record()
+        s.wait_event(ev0)
+        ple.ple_prefetch(L, dev(b.input_ids), dev(b.qsl), staging, ngram_context=dev(b.ngram_context), stream=s)
+        s.synchronize()
+        ref = ple.ple_lookup(L.hash, L.table, dev(b.input_ids), dev(b.qsl), ngram_context=dev(b.ngram_context))
+        assert torch.equal(staging, ref)
+    finally:
+        torch.cuda.synchronize()
+        ple.ple_stream_destroy(s)
