@@ -1,8 +1,9 @@
 """GPU parity of every libple entry point against the oracle, at sizes the
 oracle finishes in seconds (several tiles plus ragged tails) and on the edge
 cases of the method.  IDs, rows and fp8 dequant: bit-exact.  kv_proj: within
-one bf16 ulp.  Gate and conv bf16 outputs: max-abs 2e-2 (and at most one bf16
-ulp in practice); the fp32 gate value: rel 1e-5."""
+the fp32 dot-product error bound plus one bf16 ulp (one ulp wherever the value
+is not cancelled to near zero).  Gate and conv bf16 outputs: max-abs 2e-2 (and
+at most one bf16 ulp in practice); the fp32 gate value: rel 1e-5."""
 import json
 import os
 
@@ -236,6 +237,24 @@ def test_lookup_head_subset_matches_full():
 
 # ------------------------------------------------------------------ kv_proj
 
+def _check_kv(got, want, x, w):
+    """fp32 accumulation of K products, then one bf16 rounding: the error bound
+    is gamma_K * sum_k |x_k w_k| (gamma_K = K u / (1 - K u), u = 2^-24) plus one
+    bf16 ulp of the result.  Near zero (cancellation) this is what limits the
+    error; elsewhere the results are the correctly rounded value or a neighbour."""
+    K = x.shape[1]
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    absdot = bf16_f64(oracle.kv_proj(x & np.uint16(0x7FFF), w & np.uint16(0x7FFF))) * 1.01
+    g, e = bf16_f64(got), bf16_f64(want)
+    ulp = np.maximum(np.abs(e), 2.0 ** -126) * 2.0 ** -7
+    assert (np.abs(g - e) <= gamma * absdot + ulp).all()
+    d = bf16_ulp_distance(got, want)
+    big = np.abs(e) > 1e-2
+    assert d[big].max() <= 1
+    assert (d > 0).mean() < 0.01
+
+
 @pytest.mark.parametrize("M,K,O", [(24, 128, 256), (1, 64, 16), (300, 192, 80), (129, 128, 144),
                                    (256, 2048, 4096), (1000, 512, 1024)])
 def test_kv_proj_parity(M, K, O):
@@ -244,9 +263,7 @@ def test_kv_proj_parity(M, K, O):
     w = wl.normal_bf16((O, K), 200 + O, 12.5 / np.sqrt(K))
     want = oracle.kv_proj(x, w)
     got = host_bits(ple.ple_kv_proj(dev_bf16(x), dev_bf16(w)))
-    d = bf16_ulp_distance(got, want)
-    assert d.max() <= 1, d.max()
-    assert (d > 0).mean() < 0.01
+    _check_kv(got, want, x, w)
 
 
 def test_kv_proj_sampled_rows_at_prefill_shape():
@@ -258,8 +275,7 @@ def test_kv_proj_sampled_rows_at_prefill_shape():
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(M - 64, M),
                                      np.random.default_rng(0).integers(0, M, 64)]))
     want = oracle.kv_proj(x[rows], w)
-    d = bf16_ulp_distance(got[rows], want)
-    assert d.max() <= 1 and (d > 0).mean() < 0.01
+    _check_kv(got[rows], want, x[rows], w)
 
 
 # ------------------------------------------------------------------ gate
@@ -389,8 +405,8 @@ def test_prefill_fused_parity_small(variant):
     _, want_ctx = oracle_ids(b, want_context_out=True)
     np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
     _, st_ref = oracle.conv(ref["gated"], b.qsl, cw, cfg.conv_dilation, state=b.conv_state, want_state_out=True)
-    d = bf16_ulp_distance(host_bits(st_out), st_ref)
-    assert d.max() <= 1
+    # the carried state holds gated values (bf16 outputs of the gate)
+    assert np.abs(bf16_f64(host_bits(st_out)) - bf16_f64(st_ref)).max() <= GATE_ABS_TOL
 
 
 def test_prefill_with_prefetched_rows_equals_plain():
