@@ -93,22 +93,20 @@ def main() -> int:
     ws = torch.empty((ple.ple_prefill_workspace_bytes(layers[0], T),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(s, evs=None):
+    def timed(fn, n):
+        """Average duration of n back-to-back launches, HIP events on the launch stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def step(s):
         lay = layers[s % L]
-        if evs is not None:
-            evs[0].record()
-        ple.ple_lookup(lay.hash, lay.table, toks, qsl, rows=rows)
-        if evs is not None:
-            evs[1].record()
-        ple.ple_kv_proj(rows, lay.kv_weight, kv=kv)
-        if evs is not None:
-            evs[2].record()
-        ple.ple_gate(hidden, kv, eps=lay.eps, out=gated, want_gate=False)
-        if evs is not None:
-            evs[3].record()
-        ple.ple_conv(gated, qsl, lay.conv_weight, dilation=lay.conv_dilation, y=out)
-        if evs is not None:
-            evs[4].record()
+        ple.ple_prefill_fused(lay, toks, qsl, hidden, out=out, workspace=ws)
 
     log(f"warmup {args.warmup} steps")
     for s in range(args.warmup):
@@ -116,40 +114,30 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
-        step(args.warmup + s, evs[s])
+        step(args.warmup + s)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / K
-    stage_names = ["lookup", "kv_proj", "gate", "conv"]
-    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)]))
-                for i, n in enumerate(stage_names)}
-    gpu_step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][4]) for s in range(K)]))
 
-    # the same path through the single fused entry point
-    torch.cuda.synchronize()
-    tf0 = time.perf_counter()
-    for s in range(K):
-        lay = layers[(args.warmup + s) % L]
-        ple.ple_prefill_fused(lay, toks, qsl, hidden, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    fused_ms = (time.perf_counter() - tf0) * 1e3 / K
-
-    # lookup alone: 16 back-to-back launches over different layers (cold last-level cache)
-    lk = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    reps = 4
-    torch.cuda.synchronize()
-    lk[0].record()
-    for r in range(reps):
-        for l in range(L):
-            ple.ple_lookup(hashes[l], tb, toks, qsl, rows=rows)
-    lk[1].record()
-    torch.cuda.synchronize()
-    lookup_ms = lk[0].elapsed_time(lk[1]) / (reps * L)
+    # per-kernel durations: the same kernels, shapes and launch configurations
+    # as inside the fused step, each launched back to back
+    log("timing each kernel")
+    reps = max(K, L)
+    stage_ms = {
+        "lookup": timed(lambda i: ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=rows), 4 * L),
+        "kv_proj": timed(lambda i: ple.ple_kv_proj(rows, kv_ws[i % 4], kv=kv), reps),
+        "gate": timed(lambda i: ple.ple_gate(hidden, kv, eps=cfg.eps, out=gated, want_gate=False), reps),
+        "conv": timed(lambda i: ple.ple_conv(gated, qsl, conv_w, dilation=cfg.conv_dilation, y=out), reps),
+    }
+    lookup_ms = stage_ms["lookup"]
+    # streaming-copy ceiling: a device-to-device copy of a rows-sized buffer
+    copy_src = torch.empty_like(rows)
+    copy_ms = timed(lambda i: rows.copy_(copy_src), reps)
+    copy_gbps = 2 * rows.numel() * 2 / (copy_ms * 1e-3) / 1e9
 
     R = b.R
     lookup_bytes = T * H * D * 2 * 2 + T * 4 + (R + 1) * 4
@@ -186,12 +174,12 @@ def main() -> int:
                      "frac": round(kv_tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None},
         "lookup": {"kernel": "fused ids+gather", "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
+                   "frac_copy_ceiling": round(lookup_gbps / copy_gbps, 4),
                    "tokens_per_s": round(T / (lookup_ms * 1e-3), 1)},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_GBps": {"gate": round(gate_bytes / (stage_ms["gate"] * 1e-3) / 1e9, 1),
                         "conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)},
-        "gpu_step_ms_events": round(gpu_step_ms, 4),
-        "fused_entry_ms_per_step": round(fused_ms, 4),
+        "copy_ceiling_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -67,6 +67,7 @@ extern "C" {
 
 #define PLE_MAX_HEADS 32
 #define PLE_MAX_CONTEXT 7
+#define PLE_MAX_TOKENS (1 << 24) /* tokens per call */
 
 /*
  * Hash constants of one layer ([P3] 关键源码片段: layer multipliers, per-head
@@ -104,7 +105,7 @@ typedef struct ple_table_desc {
 typedef struct ple_batch_desc {
     const int32_t* input_ids;        /* device [T] */
     const int32_t* query_start_loc;  /* device [R+1] */
-    int64_t num_tokens;              /* T >= 0 */
+    int64_t num_tokens;              /* 0 <= T <= PLE_MAX_TOKENS */
     int32_t num_reqs;                /* R >= 0 (R == 0 requires T == 0) */
     int32_t reserved;
     const int32_t* ngram_context;    /* device [R][C], oldest first, or NULL (= all EOS) */
@@ -125,7 +126,7 @@ typedef struct ple_layer_desc {
     float eps;                   /* RMS epsilon (1e-6 in the reference workloads) */
     const uint16_t* conv_weight; /* device bf16 [N][Kc]; tap Kc-1 multiplies the current token */
     int32_t conv_kernel;         /* Kc, 1..16 */
-    int32_t conv_dilation;       /* d >= 1, (Kc-1)*d <= 64 */
+    int32_t conv_dilation;       /* d >= 1, (Kc-1)*d <= 4096 */
 } ple_layer_desc;
 
 /*
@@ -172,7 +173,8 @@ int ple_prefetch(const ple_layer_desc* layer, const ple_batch_desc* batch, uint1
  * Merged key/value projection ([P3] 实现拆解 item 1):
  *   kv[t][o] = bf16(sum_i x[t][i] * w[o][i]), fp32 accumulation, no bias.
  * x: device bf16 [T][K]; w: device bf16 [O][K]; kv: device bf16 [T][O].
- * K a multiple of 64, O a multiple of 16.
+ * K a multiple of 64, O a multiple of 16, T <= PLE_MAX_TOKENS and
+ * ceil(T/128) * ceil(O/128) <= 2^24 (else PLE_ERR_UNSUPPORTED).
  */
 int ple_kv_proj(const uint16_t* x, const uint16_t* w, int64_t num_tokens, int32_t k_dim, int32_t out_dim,
                 uint16_t* kv, void* stream);

@@ -133,8 +133,9 @@ int validate_heads_in_table(const ple_hash_desc* h, const ple_table_desc* t) {
 // Checks of the batch fields used by the ids / lookup calls.
 int validate_batch_tokens(const ple_batch_desc* b) {
     if (b == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "batch descriptor is NULL");
-    if (b->num_tokens < 0 || b->num_tokens > INT32_MAX)
-        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 0..2^31-1", (long long)b->num_tokens);
+    if (b->num_tokens < 0 || b->num_tokens > PLE_MAX_TOKENS)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 0..%d", (long long)b->num_tokens,
+                    PLE_MAX_TOKENS);
     if (b->num_reqs < 0) return fail(PLE_ERR_INVALID_ARGUMENT, "num_reqs < 0");
     if (b->num_reqs == 0 && b->num_tokens > 0)
         return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens > 0 with num_reqs == 0");
@@ -154,8 +155,9 @@ int validate_batch_tokens(const ple_batch_desc* b) {
 
 int validate_batch_conv(const ple_batch_desc* b) {
     if (b == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "batch descriptor is NULL");
-    if (b->num_tokens < 0 || b->num_tokens > INT32_MAX)
-        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 0..2^31-1", (long long)b->num_tokens);
+    if (b->num_tokens < 0 || b->num_tokens > PLE_MAX_TOKENS)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 0..%d", (long long)b->num_tokens,
+                    PLE_MAX_TOKENS);
     if (b->num_reqs < 0) return fail(PLE_ERR_INVALID_ARGUMENT, "num_reqs < 0");
     if (b->num_reqs == 0 && b->num_tokens > 0)
         return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens > 0 with num_reqs == 0");
@@ -188,9 +190,11 @@ int validate_gemm_shape(int K, int O) {
 }
 
 int validate_gemm(const uint16_t* x, const uint16_t* w, int64_t T, int K, int O, const uint16_t* kv) {
-    if (T < 0 || T > INT32_MAX) return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens outside 0..2^31-1");
+    if (T < 0 || T > PLE_MAX_TOKENS) return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens outside 0..%d", PLE_MAX_TOKENS);
     int rc = validate_gemm_shape(K, O);
     if (rc) return rc;
+    if (((T + 127) / 128) * (int64_t)((O + 127) / 128) > ((int64_t)1 << 24))
+        return fail(PLE_ERR_UNSUPPORTED, "kv_proj of %lld x %d outputs exceeds 2^24 tiles", (long long)T, O);
     if (x == nullptr || w == nullptr || kv == nullptr)
         return fail(PLE_ERR_INVALID_ARGUMENT, "kv_proj pointers must be non-NULL");
     if (!aligned16(x) || !aligned16(w) || !aligned16(kv))
@@ -200,7 +204,7 @@ int validate_gemm(const uint16_t* x, const uint16_t* w, int64_t T, int K, int O,
 
 int validate_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, const uint16_t* out,
                   const float* gate) {
-    if (T < 0 || T > INT32_MAX) return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens outside 0..2^31-1");
+    if (T < 0 || T > PLE_MAX_TOKENS) return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens outside 0..%d", PLE_MAX_TOKENS);
     if (N < 8 || N % 8 != 0) return fail(PLE_ERR_UNSUPPORTED, "hidden size %d is not a positive multiple of 8", N);
     if (!(eps >= 0.0f) || eps > 1.0f) return fail(PLE_ERR_INVALID_ARGUMENT, "eps must be in [0, 1]");
     if (hidden == nullptr || kv == nullptr || out == nullptr)
@@ -230,7 +234,7 @@ LookupArgs lookup_args(const ple_table_desc* t, int H, int cpr_log2, const ple_b
     g.num_rows = t->num_rows;
     g.num_heads = H;
     g.dim = t->dim;
-    g.tokens_per_block = lookup_tokens_per_block(T, H);
+    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dtype == PLE_DTYPE_BF16 ? t->dim / 8 : t->dim / 16);
     g.cpr_log2 = cpr_log2;
     return g;
 }
@@ -302,8 +306,8 @@ int ple_gather(const ple_table_desc* table, const int32_t* ids, int64_t num_toke
     if (rc) return rc;
     if (num_heads < 1 || num_heads > PLE_MAX_HEADS)
         return fail(PLE_ERR_INVALID_ARGUMENT, "num_heads %d outside 1..%d", num_heads, PLE_MAX_HEADS);
-    if (num_tokens < 0 || num_tokens > INT32_MAX)
-        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens outside 0..2^31-1");
+    if (num_tokens < 0 || num_tokens > PLE_MAX_TOKENS)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens outside 0..%d", PLE_MAX_TOKENS);
     if (num_tokens == 0) return ok();
     if (ids == nullptr || !aligned4(ids)) return fail(PLE_ERR_INVALID_ARGUMENT, "ids is NULL or misaligned");
     if (rows == nullptr || !aligned16(rows)) return fail(PLE_ERR_INVALID_ARGUMENT, "rows is NULL or not 16-byte aligned");

@@ -84,4 +84,53 @@ __device__ __forceinline__ uint32_t floor_mod_wrapped(uint64_t acc, uint32_t V, 
     return rr;
 }
 
+// Request index r and clamped start a of token t (this lane's token, the
+// k-th of the wave's `ntok` consecutive tokens starting at t_first).  The wave
+// loads query_start_loc cooperatively (one load per lane per 64 entries, all
+// in flight together) and counts the entries <= each token with ballots, so
+// finding the request costs one memory round trip instead of a chain of
+// dependent binary-search loads.  Every lane of the wave must call this.
+__device__ __forceinline__ void wave_find_request(const int32_t* __restrict__ qsl, int R, int64_t t,
+                                                  int64_t t_first, int ntok, int my_k, int lane, int& r_out,
+                                                  int64_t& a_out) {
+    int r;
+    int64_t a;
+    if (R + 1 <= kWave) {
+        const int q = lane <= R ? qsl[lane] : 0;
+        r = 0;
+        for (int k = 0; k < ntok; ++k) {
+            const int64_t tk = t_first + k;
+            const uint64_t m = __ballot(lane >= 1 && lane <= R && (int64_t)q <= tk);
+            const int rk = min(__popcll(m), R - 1);
+            if (k == my_k) r = rk;
+        }
+        a = __shfl(q, r, kWave);
+    } else if (R <= 16 * kWave) {
+        int q[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int idx = 1 + c * kWave + lane;
+            q[c] = (idx <= R) ? qsl[idx] : 0;
+        }
+        int cnt = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int idx = 1 + c * kWave + lane;
+            if (1 + c * kWave <= R) {  // wave-uniform
+                for (int k = 0; k < ntok; ++k) {
+                    const uint64_t m = __ballot(idx <= R && (int64_t)q[c] <= t_first + k);
+                    if (k == my_k) cnt += __popcll(m);
+                }
+            }
+        }
+        r = min(cnt, R - 1);
+        a = qsl[r];
+    } else {
+        r = find_request(qsl, R, t);
+        a = qsl[r];
+    }
+    r_out = r;
+    a_out = a < 0 ? 0 : (a > t ? t : a);  // keeps every read in bounds for any qsl
+}
+
 }  // namespace ple

@@ -6,12 +6,20 @@
 //
 // Gate: one wave per token; each lane keeps fp32 partial sums of h.h, k.k and
 // h.k over its 16-byte chunks, the wave reduces them in double, and the same
-// wave then scales the value half.  Conv: one lane per (token, 8 channels),
-// taps read as 16-byte chunks from the token rows t, t-d, ... (re-reads hit
-// L2, so HBM sees each row about once), state rows before a request start.
+// wave then scales the value half.  Conv: blocks of 16 tokens x 256 chunks of
+// 8 channels; request starts found once per block; each lane issues all the
+// tap loads of 4 tokens (16-byte chunks of rows t, t-d, ...) before using
+// them; re-reads hit L2, so HBM sees each row about once; taps before a
+// request's start come from the carried state.
 #include "ple_launch.h"
 
+#ifndef PLE_CONV_TOKENS_PER_BLOCK
+#define PLE_CONV_TOKENS_PER_BLOCK 32
+#endif
+
 namespace ple {
+
+constexpr int kConvKMax = 8;  // kernel sizes above this use the generic kernel
 
 __device__ __forceinline__ void acc_dot(u32x4 a, u32x4 b, float& aa, float& bb, float& ab) {
     const uint32_t x[4] = {a.x, a.y, a.z, a.w};
@@ -164,6 +172,317 @@ __global__ __launch_bounds__(256) void conv_kernel(const uint16_t* __restrict__ 
     }
 }
 
+// Tiled convolution for compile-time kernel sizes.  A block covers TB
+// consecutive tokens x 256 chunks of 8 channels.  Wave 0 finds the request of
+// each of the TB tokens with one cooperative load of query_start_loc and puts
+// (request, start) in LDS; then every lane walks its channel chunk through the
+// TB tokens, TT tokens at a time, issuing all TT x KC tap loads before using
+// any (16 loads in flight per lane for KC = 4).  Rows re-read by neighbouring
+// tokens hit L2, so HBM sees each input row about once.
+template <int KC, int TB, int TT>
+__global__ __launch_bounds__(256) void conv_tile_kernel(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ qsl, int64_t T, int R,
+                                                        const uint16_t* __restrict__ state,
+                                                        const uint16_t* __restrict__ w, int N, int d,
+                                                        uint16_t* __restrict__ y) {
+    __shared__ int32_t s_r[TB];
+    __shared__ int64_t s_a[TB];
+    const int tid = threadIdx.x;
+    const int nch = N >> 3;
+    const int64_t t0 = (int64_t)blockIdx.x * TB;
+    const int nt = (int)min((int64_t)TB, T - t0);
+    const int64_t S = (int64_t)(KC - 1) * d;
+    if (tid < kWave) {
+        const int my_k = tid < nt ? tid : 0;
+        int r;
+        int64_t a;
+        wave_find_request(qsl, R, t0 + my_k, t0, nt, my_k, tid, r, a);
+        if (tid < nt) {
+            s_r[tid] = r;
+            s_a[tid] = a;
+        }
+    }
+    __syncthreads();
+
+    const int c = blockIdx.y * 256 + tid;
+    if (c >= nch) return;  // no barrier below
+    const int c0 = c * 8;
+    float wt[8][KC];
+    {
+        const u32x4* wp = (const u32x4*)(w + (int64_t)c0 * KC);
+        uint32_t words[4 * KC];
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            const u32x4 v4 = wp[q];
+            words[4 * q] = v4.x; words[4 * q + 1] = v4.y; words[4 * q + 2] = v4.z; words[4 * q + 3] = v4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int k = 0; k < KC; ++k) {
+                const int flat = e * KC + k;
+                wt[e][k] = (flat & 1) ? bf16_hi(words[flat >> 1]) : bf16_lo(words[flat >> 1]);
+            }
+    }
+
+    for (int k0 = 0; k0 < nt; k0 += TT) {
+        u32x4 xv[TT][KC];
+#pragma unroll
+        for (int kk = 0; kk < TT; ++kk) {
+            const int k = k0 + kk;
+            const bool valid = k < nt;
+            const int kc = valid ? k : 0;
+            const int64_t t = t0 + kc;
+            const int64_t a = s_a[kc];
+            const int r = s_r[kc];
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                const int64_t p = t - (int64_t)i * d;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (valid) {
+                    if (p >= a)
+                        v = *(const u32x4*)(x + p * N + c0);
+                    else if (state != nullptr)
+                        v = *(const u32x4*)(state + ((int64_t)r * S + (S - (a - p))) * N + c0);
+                }
+                xv[kk][i] = v;
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < TT; ++kk) {
+            const int k = k0 + kk;
+            if (k < nt) {
+                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < KC; ++i) {
+                    float f[8];
+                    unpack8(xv[kk][i], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += wt[e][KC - 1 - i] * f[e];
+                }
+                *(u32x4*)(y + (t0 + k) * N + c0) =
+                    u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                          pack_bf16x2(acc[6], acc[7])};
+            }
+        }
+    }
+}
+
+// LDS-staged convolution.  A block covers TB consecutive tokens x 64 chunks of
+// 8 channels (1 KiB of each row).  It stages the rows [t0 - S, t0 + TB) of its
+// channel slice in LDS once (every input element is read from HBM once, plus
+// an S-row halo per tile), wave 0 finds each token's request with one
+// cooperative load of query_start_loc, then lane c of each wave produces
+// channel chunk c for every 4th token, reading its taps from LDS.  Taps that
+// fall before the token's request start come from the carried state (a
+// global read, only near request starts) or are zero.
+template <int TB>
+__global__ __launch_bounds__(256) void conv_lds_kernel(const uint16_t* __restrict__ x,
+                                                       const int32_t* __restrict__ qsl, int64_t T, int R,
+                                                       const uint16_t* __restrict__ state,
+                                                       const uint16_t* __restrict__ w, int N, int K, int d,
+                                                       uint16_t* __restrict__ y) {
+    extern __shared__ u32x4 s_x[];  // (TB + S) rows x 64 chunks
+    __shared__ uint16_t s_w[kWave * 8 * kConvKMax];  // this slice's weights, [channel][tap]
+    __shared__ int32_t s_r[TB];
+    __shared__ int64_t s_a[TB];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid >> 6;
+    const int nch = N >> 3;
+    // the channel slice varies fastest with the block id, so the slices of one
+    // token tile are adjacent block ids: together they touch whole rows at once, and with
+    // block ids dealt round-robin to the 8 XCDs each XCD keeps one slice (and
+    // the halo rows it shares with the previous tile) in its own L2
+    const int nslice = (nch + kWave - 1) / kWave;
+    const int64_t t0 = (int64_t)(blockIdx.x / nslice) * TB;
+    const int nt = (int)min((int64_t)TB, T - t0);
+    const int S = (K - 1) * d;
+    const int c = (int)(blockIdx.x % nslice) * kWave + lane;  // this lane's channel chunk
+    const bool cvalid = c < nch;
+
+    // stage rows t0 - S .. t0 + nt - 1 (row index in LDS: p - (t0 - S))
+    const int nrow = nt + S;
+    for (int i = wv; i < nrow; i += 4) {
+        const int64_t p = t0 - S + i;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (p >= 0 && cvalid) v = *(const u32x4*)(x + p * N + (int64_t)c * 8);
+        s_x[i * kWave + lane] = v;
+    }
+    {
+        // the slice's 512 channels x K taps are contiguous in w: 64*K 16-byte chunks
+        const int slice_c0 = (int)(blockIdx.x % nslice) * kWave * 8;
+        const int nchunk = min(kWave, nch - (int)(blockIdx.x % nslice) * kWave) * K;
+        const u32x4* wsrc = (const u32x4*)(w + (int64_t)slice_c0 * K);
+        for (int i = tid; i < nchunk; i += 256) ((u32x4*)s_w)[i] = wsrc[i];
+    }
+    if (wv == 0) {
+        const int my_k = lane < nt ? lane : 0;
+        int r;
+        int64_t a;
+        wave_find_request(qsl, R, t0 + my_k, t0, nt, my_k, lane, r, a);
+        if (lane < nt) {
+            s_r[lane] = r;
+            s_a[lane] = a;
+        }
+    }
+    __syncthreads();
+    if (!cvalid) return;  // no barrier below
+
+    const int c0 = c * 8;
+    // this lane's 8 channels x K taps, tap order reversed: wt[e][i] multiplies x(t - i*d)
+    float wt[8][kConvKMax];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < kConvKMax; ++i)
+            wt[e][i] = i < K ? __uint_as_float((uint32_t)s_w[(lane * 8 + e) * K + (K - 1 - i)] << 16) : 0.f;
+    for (int k = wv; k < nt; k += 4) {
+        const int64_t t = t0 + k;
+        const int64_t a = s_a[k];
+        const int r = s_r[k];
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kConvKMax; ++i) {
+            if (i < K) {
+                const int64_t p = t - (int64_t)i * d;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (p >= a)
+                    v = s_x[(int)(p - (t0 - S)) * kWave + lane];
+                else if (state != nullptr)
+                    v = *(const u32x4*)(state + ((int64_t)r * S + (S - (a - p))) * N + c0);
+                float f[8];
+                unpack8(v, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += wt[e][i] * f[e];
+            }
+        }
+        *(u32x4*)(y + t * N + c0) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                          pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    }
+}
+
+// Persistent row-wise convolution for compile-time kernel sizes (the fast
+// path).  Each block stages all N x KC weights in LDS once, then its waves
+// walk tokens: a wave produces one whole output row at a time.  Tokens are
+// dealt so that each XCD (block id mod 8) owns a contiguous token range and
+// its waves work on neighbouring tokens together; the tap rows t-d, t-2d, ...
+// a wave reads were just read by its neighbours, so they come from that XCD's
+// L2 and HBM sees each input row about once.  The tap loads are issued
+// speculatively together with the request lookup (one round trip); taps that
+// fall before the request start are then replaced by the carried state (or
+// zero).
+template <int KC>
+__global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ qsl, int64_t T, int R,
+                                                        const uint16_t* __restrict__ state,
+                                                        const uint16_t* __restrict__ w, int N, int d,
+                                                        uint16_t* __restrict__ y) {
+    // weights [N][KC] = nch x KC 16-byte chunks, kept in LDS tap-chunk-major
+    // (s_wv[q * nch + c]) so that consecutive lanes read consecutive chunks
+    extern __shared__ u32x4 s_wv[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid >> 6;
+    const int nch = N >> 3;
+    for (int i = tid; i < nch * KC; i += 256) {
+        const int c = i / KC, q = i - (i / KC) * KC;
+        s_wv[q * nch + c] = ((const u32x4*)w)[i];
+    }
+    __syncthreads();
+
+    const int64_t S = (int64_t)(KC - 1) * d;
+    const int xcd = blockIdx.x & 7;
+    const int64_t blocks_per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
+    const int64_t per_xcd = (T + 7) / 8;
+    const int64_t t_begin = xcd * per_xcd;
+    const int64_t t_end = min(T, t_begin + per_xcd);
+    const int64_t stride = blocks_per_xcd * 4;
+    constexpr int CPL = 4;  // 16-byte chunks per lane per pass
+
+    for (int64_t t = t_begin + (int64_t)(blockIdx.x >> 3) * 4 + wv; t < t_end; t += stride) {
+        int r = 0;
+        int64_t a = 0;
+        for (int cb = 0; cb < nch; cb += kWave * CPL) {
+            u32x4 xv[CPL][KC];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = cb + j * kWave + lane;
+#pragma unroll
+                for (int i = 0; i < KC; ++i) {
+                    const int64_t p = t - (int64_t)i * d;
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (c < nch && p >= 0) v = *(const u32x4*)(x + p * N + (int64_t)c * 8);
+                    xv[j][i] = v;
+                }
+            }
+            if (cb == 0) wave_find_request(qsl, R, t, t, 1, 0, lane, r, a);  // wave-uniform branch
+#pragma unroll
+            for (int i = 1; i < KC; ++i) {
+                const int64_t p = t - (int64_t)i * d;
+                if (p < a) {  // wave-uniform: before this request's first token
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        const int c = cb + j * kWave + lane;
+                        u32x4 v = {0u, 0u, 0u, 0u};
+                        if (state != nullptr && c < nch)
+                            v = *(const u32x4*)(state + ((int64_t)r * S + (S - (a - p))) * N + (int64_t)c * 8);
+                        xv[j][i] = v;
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = cb + j * kWave + lane;
+                if (c < nch) {
+                    uint32_t wd[4 * KC];
+#pragma unroll
+                    for (int q = 0; q < KC; ++q) {
+                        const u32x4 v4 = s_wv[q * nch + c];
+                        wd[4 * q] = v4.x; wd[4 * q + 1] = v4.y; wd[4 * q + 2] = v4.z; wd[4 * q + 3] = v4.w;
+                    }
+                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < KC; ++i) {
+                        float f[8];
+                        unpack8(xv[j][i], f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int flat = e * KC + (KC - 1 - i);  // w[c*8+e][KC-1-i]
+                            const float wt = (flat & 1) ? bf16_hi(wd[flat >> 1]) : bf16_lo(wd[flat >> 1]);
+                            acc[e] += wt * f[e];
+                        }
+                    }
+                    *(u32x4*)(y + t * N + (int64_t)c * 8) =
+                        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                              pack_bf16x2(acc[6], acc[7])};
+                }
+            }
+        }
+    }
+}
+
+template <int KC>
+static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
+                                   const uint16_t* w, int N, int d, uint16_t* y, hipStream_t s) {
+    const size_t lds = (size_t)N * KC * 2;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)conv_rows_kernel<KC>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+    if (attr != hipSuccess) return attr;
+    int dev = 0, cus = 256, per_cu = 1;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC>, 256, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    int64_t blocks = (int64_t)cus * per_cu;                  // every block resident at once
+    const int64_t need = (T + 3) / 4;                        // one wave per token at most
+    if (blocks > need) blocks = need;
+    blocks = ((blocks + 7) / 8) * 8;                         // whole XCD rounds
+    hipLaunchKernelGGL((conv_rows_kernel<KC>), dim3((unsigned)blocks), dim3(256), lds, s, x, qsl, T, R, state, w, N,
+                       d, y);
+    return hipGetLastError();
+}
+
 // state_out[r][m] = the (S-m)-th most recent conv input of state[r] ++ x[a:b].
 __global__ __launch_bounds__(256) void conv_state_out_kernel(const uint16_t* __restrict__ x,
                                                              const int32_t* __restrict__ qsl, int64_t T, int R,
@@ -199,16 +518,31 @@ hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, in
 
 hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
                        const uint16_t* w, int N, int K, int d, uint16_t* y, hipStream_t s) {
-    const int64_t total = T * (N >> 3);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > (1 << 20)) blocks = 1 << 20;
-    dim3 g((unsigned)blocks), b(256);
-    switch (K) {
-        case 1: hipLaunchKernelGGL(conv_kernel<1>, g, b, 0, s, x, qsl, T, R, state, w, N, K, d, y); break;
-        case 2: hipLaunchKernelGGL(conv_kernel<2>, g, b, 0, s, x, qsl, T, R, state, w, N, K, d, y); break;
-        case 3: hipLaunchKernelGGL(conv_kernel<3>, g, b, 0, s, x, qsl, T, R, state, w, N, K, d, y); break;
-        case 4: hipLaunchKernelGGL(conv_kernel<4>, g, b, 0, s, x, qsl, T, R, state, w, N, K, d, y); break;
-        default: hipLaunchKernelGGL(conv_kernel<0>, g, b, 0, s, x, qsl, T, R, state, w, N, K, d, y); break;
+    if ((size_t)N * K * 2 <= 64 * 1024) {
+        switch (K) {
+            case 1: return launch_conv_rows<1>(x, qsl, T, R, state, w, N, d, y, s);
+            case 2: return launch_conv_rows<2>(x, qsl, T, R, state, w, N, d, y, s);
+            case 3: return launch_conv_rows<3>(x, qsl, T, R, state, w, N, d, y, s);
+            case 4: return launch_conv_rows<4>(x, qsl, T, R, state, w, N, d, y, s);
+            default: break;
+        }
+    }
+    constexpr int TB = PLE_CONV_TOKENS_PER_BLOCK;
+    const int nch = N >> 3;
+    const int S = (K - 1) * d;
+    const size_t lds = (size_t)(TB + S) * kWave * 16;
+    if (lds <= 96 * 1024 && K <= kConvKMax) {
+        static const hipError_t attr = hipFuncSetAttribute((const void*)conv_lds_kernel<TB>,
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+        if (attr != hipSuccess) return attr;
+        dim3 g((unsigned)(((nch + kWave - 1) / kWave) * ((T + TB - 1) / TB)));
+        hipLaunchKernelGGL((conv_lds_kernel<TB>), g, dim3(256), lds, s, x, qsl, T, R, state, w, N, K, d, y);
+    } else {
+        const int64_t total = T * nch;
+        int64_t blocks = (total + 255) / 256;
+        if (blocks > (1 << 20)) blocks = 1 << 20;
+        hipLaunchKernelGGL(conv_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, x, qsl, T, R, state, w, N, K, d,
+                           y);
     }
     return hipGetLastError();
 }

@@ -177,17 +177,158 @@ __global__ __launch_bounds__(256) void kv_proj_kernel(const uint16_t* __restrict
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-problem kernel: 256 x 256 x 64 block tile, 4 waves of 128 x 128.
+//
+// Operands go global -> LDS with the gfx950 direct-to-LDS 16-byte loads
+// (global_load_lds_dwordx4): no register staging, and the copy of the next
+// K-slice runs while the MFMAs consume the current one (two LDS stages).  One
+// wave instruction fills 1 KiB of LDS = 8 rows x 8 16-byte chunks; each lane
+// picks the global chunk so that LDS holds chunk (row, kc) at position
+// row*8 + (kc ^ ((row >> 1) & 7)).  An MFMA fragment read takes one k-chunk
+// of 32 consecutive rows; the LDS serves 16 lanes (256 bytes, 64 banks) per
+// cycle, and with this swizzle any 16 consecutive rows land on 16 distinct
+// 16-byte bank groups (row parity picks the half, (row >> 1) & 7 the group).  The MFMA operands are swapped (W fragment first)
+// so each lane's accumulators are 4 consecutive output features of one token,
+// which the epilogue writes to LDS as 8-byte pairs before the coalesced
+// 16-byte global stores.
+// ---------------------------------------------------------------------------
+constexpr int kBigTile = 256;
+constexpr int kBigStageBytes = 2 * kBigTile * kBK * 2;          // A + B slices: 64 KiB
+constexpr int kBigOutRow = kBigTile + 8;                         // epilogue row (elements)
+constexpr int kBigLdsBytes = (2 * kBigStageBytes > kBigTile * kBigOutRow * 2) ? 2 * kBigStageBytes
+                                                                              : kBigTile * kBigOutRow * 2;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ ((row >> 1) & 7)); }
+
+__global__ __launch_bounds__(256, 1) void kv_proj_big_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ w, int M, int K, int O,
+                                                             uint16_t* __restrict__ out) {
+    extern __shared__ __align__(16) char lds_raw[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int tiles_m = (M + kBigTile - 1) / kBigTile;
+    const int tiles_n = (O + kBigTile - 1) / kBigTile;
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kBigTile, n0 = tn * kBigTile;
+
+    // per-lane source rows for the 8 load instructions of each operand:
+    // instruction i of wave `wave` fills rows g*8 .. g*8+7 with g = i*4 + wave
+    // lane L writes LDS position group*64 + L = row*8 + (kc ^ ((row >> 1) & 7)),
+    // row = group*8 + L/8: it fetches global chunk kc = (L & 7) ^ ((row >> 1) & 7)
+    const int lrow = lane >> 3;  // row within the 8-row group
+    const uint16_t* asrc[8];
+    const uint16_t* bsrc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = (i * 4 + wave) * 8 + lrow;
+        const int lkc = (lane & 7) ^ ((row >> 1) & 7);
+        asrc[i] = x + (int64_t)min(m0 + row, M - 1) * K + lkc * 8;
+        bsrc[i] = w + (int64_t)min(n0 + row, O - 1) * K + lkc * 8;
+    }
+    auto issue_slice = [&](int kt, int stage) {
+        char* base = lds_raw + stage * kBigStageBytes;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int g = i * 4 + wave;
+            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * kBK), (lds_ptr_t)(base + g * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + kt * kBK),
+                                             (lds_ptr_t)(base + kBigTile * kBK * 2 + g * 1024), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];  // [W sub-tile j][x sub-tile i]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
+
+    const int nk = K / kBK;
+    issue_slice(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    const int frow = lane & 31;
+    const int fk = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < nk) issue_slice(kt + 1, stage ^ 1);
+        const u32x4* As = (const u32x4*)(lds_raw + stage * kBigStageBytes);
+        const u32x4* Bs = As + kBigTile * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int kc = kk * 2 + fk;
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * 128 + i * 32 + frow;
+                af[i] = __builtin_bit_cast(bf16x8, As[swz(row, kc)]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wn * 128 + j * 32 + frow;
+                bfr[j] = __builtin_bit_cast(bf16x8, Bs[swz(row, kc)]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this lane's copies of the next slice have landed
+        __syncthreads();                     // ... and everyone's; the current stage is free again
+    }
+
+    // epilogue: acc[j][i][e] is feature n0 + wn*128 + j*32 + 8*(e/4) + 4*(lane/32) + e%4
+    // of token m0 + wm*128 + i*32 + lane%32
+    uint16_t* Cs = (uint16_t*)lds_raw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int m = wm * 128 + i * 32 + frow;
+                const int o = wn * 128 + j * 32 + 8 * g + 4 * fk;
+                const uint32_t lo = pack_bf16x2(acc[j][i][4 * g], acc[j][i][4 * g + 1]);
+                const uint32_t hi = pack_bf16x2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
+                *(uint2*)(Cs + m * kBigOutRow + o) = make_uint2(lo, hi);
+            }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = tid; c < kBigTile * kBigTile / 8; c += 256) {
+        const int row = c >> 5;           // 32 chunks of 8 features per row
+        const int col = (c & 31) * 8;
+        const int gr = m0 + row, gc = n0 + col;
+        if (gr < M && gc < O) *(u32x4*)(out + (int64_t)gr * O + gc) = *(const u32x4*)(Cs + row * kBigOutRow + col);
+    }
+}
+
+static hipError_t launch_kv_proj_big(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
+                                     hipStream_t s) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)kv_proj_big_kernel,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsBytes);
+    if (attr != hipSuccess) return attr;
+    const int tiles = (int)((M + kBigTile - 1) / kBigTile) * ((O + kBigTile - 1) / kBigTile);
+    hipLaunchKernelGGL(kv_proj_big_kernel, dim3(tiles), dim3(256), kBigLdsBytes, s, x, w, (int)M, K, O, kv);
+    return hipGetLastError();
+}
+
 template <int BM, int BN>
 static hipError_t launch_kv_proj_t(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                                    hipStream_t s) {
     using S = GemmShape<BM, BN>;
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute((const void*)kv_proj_kernel<BM, BN>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static const hipError_t attr = hipFuncSetAttribute((const void*)kv_proj_kernel<BM, BN>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
     const int tiles = (int)((M + BM - 1) / BM) * ((O + BN - 1) / BN);
     hipLaunchKernelGGL((kv_proj_kernel<BM, BN>), dim3(tiles), dim3(256), S::LDS_BYTES, s, x, w, (int)M, K, O, kv);
     return hipGetLastError();
@@ -195,6 +336,9 @@ static hipError_t launch_kv_proj_t(const uint16_t* x, const uint16_t* w, int64_t
 
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s) {
+    // 256 x 256 tiles when they alone fill the chip; 128 x 128 otherwise
+    const int64_t big_tiles = ((M + kBigTile - 1) / kBigTile) * ((O + kBigTile - 1) / kBigTile);
+    if (big_tiles >= 256) return launch_kv_proj_big(x, w, M, K, O, kv, s);
     return launch_kv_proj_t<128, 128>(x, w, M, K, O, kv, s);
 }
 

@@ -8,57 +8,31 @@
 // memory); FP8 e4m3fn tables with a scale from "Support PLE-Offload for
 // Qwen3.8-Flash-Next - #53899".
 //
-// Design for CDNA4: one lane per (token, head) pair computes the ID in
-// registers (binary search over query_start_loc, window from the token
-// array, Barrett reduction instead of a 64-bit divide); the IDs of a block's
-// tokens stay in LDS and the block then streams its rows with 16-byte loads
-// (one wave instruction moves a whole 1 KiB bf16 row), many loads in flight
-// per lane, and coalesced 16-byte stores into the contiguous [tokens][H*D]
-// output slab of the block.
+// Design for CDNA4: each wave owns a few consecutive tokens (at most 64
+// (token, head) rows).  One lane per row computes the ID in registers: the
+// wave finds request boundaries with one cooperative load of query_start_loc
+// and ballots, the window tokens are loaded in the same round trip, and the
+// modulo is a Barrett reduction instead of a 64-bit divide.  The IDs never
+// leave registers: the wave then streams its rows with 16-byte loads (one wave
+// instruction moves a whole 1 KiB bf16 row; the row's ID comes from the
+// owning lane by a cross-lane read), 16 loads in flight per lane, and writes
+// coalesced 16-byte chunks into the wave's contiguous [tokens][H*D] slab.
+// Waves never wait for each other.
 #include "ple_launch.h"
 
+// Tuning knobs (compile-time): 16-byte loads in flight per lane, and whether
+// table reads / row writes carry the non-temporal hint.
+#ifndef PLE_LOOKUP_LOADS
+#define PLE_LOOKUP_LOADS 16
+#endif
+#ifndef PLE_LOOKUP_NT_LOAD
+#define PLE_LOOKUP_NT_LOAD 1
+#endif
+#ifndef PLE_LOOKUP_NT_STORE
+#define PLE_LOOKUP_NT_STORE 0
+#endif
+
 namespace ple {
-
-__device__ __forceinline__ int32_t pair_id(const HashParams& hp, const int32_t* __restrict__ tok,
-                                           const int32_t* __restrict__ qsl, int R,
-                                           const int32_t* __restrict__ ctx, int64_t t, int h) {
-    const int r = find_request(qsl, R, t);
-    int64_t a = qsl[r];
-    a = a < 0 ? 0 : (a > t ? t : a);  // keeps every read in bounds for any qsl
-    const int C = hp.context_len;
-    const int32_t eos = hp.eos;
-    const int order = hp.order[h];
-    uint64_t acc = (uint64_t)(int64_t)tok[t] * hp.mult[h][0];
-    bool crossed = false;
-    for (int j = 1; j < order; ++j) {
-        const int64_t p = t - j;
-        int32_t raw;
-        if (p >= a)
-            raw = tok[p];
-        else if (ctx != nullptr)
-            raw = ctx[(int64_t)r * C + (C - (a - p))];
-        else
-            raw = eos;
-        crossed |= (raw == eos);
-        const int64_t s = crossed ? (int64_t)eos : (int64_t)raw;
-        acc += (uint64_t)s * hp.mult[h][j];
-    }
-    return (int32_t)(hp.offset[h] + floor_mod_wrapped(acc, hp.vocab[h], hp.barrett[h], hp.wrap_mod[h]));
-}
-
-__global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int32_t* __restrict__ tok,
-                                                        const int32_t* __restrict__ qsl, int64_t T, int R,
-                                                        const int32_t* __restrict__ ctx,
-                                                        int32_t* __restrict__ ids) {
-    const int H = hp.num_heads;
-    const int64_t total = T * H;
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
-         p += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t t = p / H;
-        const int h = (int)(p - t * H);
-        ids[p] = pair_id(hp, tok, qsl, R, ctx, t, h);
-    }
-}
 
 // Carried context: out[r][i] = the (C-i)-th most recent raw token of ctx[r] ++ tok[a:b].
 __global__ __launch_bounds__(256) void context_out_kernel(const int32_t* __restrict__ tok,
@@ -101,34 +75,78 @@ __device__ __forceinline__ void dequant16(u32x4 q, float scale, u32x4& lo, u32x4
     hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
-// One block: `tb` tokens x H heads.  Phase 1 puts the block's row IDs (and
-// fp8 scales) in LDS; phase 2 streams the rows.  MODE_HASH computes the IDs,
-// MODE_IDS reads (and clamps) caller IDs.
+// ID of head h for token t, given its request (r, a) and the raw tokens
+// w[j] = tok[max(t-j, 0)] loaded ahead (the value is used only when t-j >= a).
+__device__ __forceinline__ int32_t window_id(const HashParams& hp, const int32_t (&w)[PLE_MAX_CONTEXT + 1],
+                                             const int32_t* __restrict__ ctx, int r, int64_t a, int64_t t, int h) {
+    const int C = hp.context_len;
+    const int32_t eos = hp.eos;
+    const int order = hp.order[h];
+    uint64_t acc = (uint64_t)(int64_t)w[0] * hp.mult[h][0];
+    bool crossed = false;
+#pragma unroll
+    for (int j = 1; j <= PLE_MAX_CONTEXT; ++j) {
+        if (j < order) {
+            const int64_t p = t - j;
+            int32_t raw;
+            if (p >= a)
+                raw = w[j];
+            else if (ctx != nullptr)
+                raw = ctx[(int64_t)r * C + (C - (a - p))];
+            else
+                raw = eos;
+            crossed |= (raw == eos);
+            const int64_t sj = crossed ? (int64_t)eos : (int64_t)raw;
+            acc += (uint64_t)sj * hp.mult[h][j];
+        }
+    }
+    return (int32_t)(hp.offset[h] + floor_mod_wrapped(acc, hp.vocab[h], hp.barrett[h], hp.wrap_mod[h]));
+}
+
+__device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
+#if PLE_LOOKUP_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// One wave: `tokens_per_wave` consecutive tokens x H heads = at most 64 rows,
+// one lane per (token, head) pair for the IDs.  No block-level barrier: each
+// wave computes its IDs and streams its rows on its own.  MODE_HASH computes
+// the IDs, MODE_IDS reads (and clamps) caller IDs.
 template <int DTYPE, int MODE, int UNROLL>
 __global__ __launch_bounds__(256) void lookup_kernel(HashParams hp, LookupArgs g) {
-    __shared__ int32_t s_id[256];
-    __shared__ float s_scale[256];
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int TW = g.tokens_per_wave;
+    const int64_t t0 = wave * TW;
+    if (t0 >= g.num_tokens) return;  // whole wave
     const int H = g.num_heads;
-    const int64_t t0 = (int64_t)blockIdx.x * g.tokens_per_block;
-    const int nt = (int)min((int64_t)g.tokens_per_block, g.num_tokens - t0);
+    const int nt = (int)min((int64_t)TW, g.num_tokens - t0);
     const int nrows = nt * H;
+    const bool active = lane < nrows;
+    const int my_k = active ? lane / H : 0;
+    const int h = active ? lane - my_k * H : 0;
+    const int64_t t = t0 + my_k;
 
-    if (tid < nrows) {
-        int32_t id;
-        if (MODE == kModeHash) {
-            const int i = tid / H;
-            const int h = tid - i * H;
-            id = pair_id(hp, g.tok, g.qsl, g.num_reqs, g.ctx, t0 + i, h);
-            if (g.ids_out != nullptr) g.ids_out[t0 * H + tid] = id;
-        } else {
-            id = g.ids_in[t0 * H + tid];
-            id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
-        }
-        s_id[tid] = id;
-        if (DTYPE == PLE_DTYPE_FP8_E4M3) s_scale[tid] = g.scales[id];
+    int32_t id = 0;
+    if (MODE == kModeHash) {
+        int32_t w[PLE_MAX_CONTEXT + 1];
+#pragma unroll
+        for (int j = 0; j <= PLE_MAX_CONTEXT; ++j)
+            w[j] = (j <= hp.context_len) ? g.tok[t - j >= 0 ? t - j : 0] : 0;
+        int r;
+        int64_t a;
+        wave_find_request(g.qsl, g.num_reqs, t, t0, nt, my_k, lane, r, a);
+        id = window_id(hp, w, g.ctx, r, a, t, h);
+        if (active && g.ids_out != nullptr) g.ids_out[t0 * H + lane] = id;
+    } else {
+        id = active ? g.ids_in[t0 * H + lane] : 0;
+        id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
     }
-    __syncthreads();
+    float scale = 0.f;
+    if (DTYPE == PLE_DTYPE_FP8_E4M3) scale = g.scales[id];
 
     // chunks of 16 input bytes per row: D*2/16 for bf16, D/16 for fp8
     const int cpr = DTYPE == PLE_DTYPE_BF16 ? (g.dim >> 3) : (g.dim >> 4);
@@ -138,34 +156,71 @@ __global__ __launch_bounds__(256) void lookup_kernel(HashParams hp, LookupArgs g
     const int64_t row_bytes = DTYPE == PLE_DTYPE_BF16 ? (int64_t)g.dim * 2 : (int64_t)g.dim;
     u32x4* __restrict__ out = (u32x4*)(g.rows + t0 * H * (int64_t)g.dim);
 
-    for (int base = tid; base < total; base += 256 * UNROLL) {
+    for (int base = 0; base < total; base += kWave * UNROLL) {
         u32x4 v[UNROLL];
-        int rowi[UNROLL];
+        float sc[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int idx = base + u * 256;
+            const int idx = base + u * kWave + lane;
+            int row = shift >= 0 ? (idx >> shift) : (idx / cpr);
+            row = row < nrows ? row : nrows - 1;
+            const int rid = __shfl(id, row, kWave);
+            if (DTYPE == PLE_DTYPE_FP8_E4M3) sc[u] = __shfl(scale, row, kWave);
             if (idx < total) {
-                const int row = shift >= 0 ? (idx >> shift) : (idx / cpr);
                 const int ch = idx - row * cpr;
-                rowi[u] = row;
-                const u32x4* src = (const u32x4*)(table + (int64_t)s_id[row] * row_bytes) + ch;
+                const u32x4* src = (const u32x4*)(table + (int64_t)rid * row_bytes) + ch;
+#if PLE_LOOKUP_NT_LOAD
                 v[u] = __builtin_nontemporal_load(src);
+#else
+                v[u] = *src;
+#endif
             }
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int idx = base + u * 256;
+            const int idx = base + u * kWave + lane;
             if (idx < total) {
                 if (DTYPE == PLE_DTYPE_BF16) {
-                    out[idx] = v[u];
+                    store16(out + idx, v[u]);
                 } else {
                     u32x4 lo, hi;
-                    dequant16(v[u], s_scale[rowi[u]], lo, hi);
-                    out[2 * idx] = lo;
-                    out[2 * idx + 1] = hi;
+                    dequant16(v[u], sc[u], lo, hi);
+                    store16(out + 2 * idx, lo);
+                    store16(out + 2 * idx + 1, hi);
                 }
             }
         }
+    }
+}
+
+// IDs only: the lookup kernel's first phase.  Each wave takes 64/H
+// consecutive tokens (one lane per (token, head)) and writes their IDs as one
+// coalesced store.
+__global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int32_t* __restrict__ tok,
+                                                        const int32_t* __restrict__ qsl, int64_t T, int R,
+                                                        const int32_t* __restrict__ ctx,
+                                                        int32_t* __restrict__ ids) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int H = hp.num_heads;
+    const int TW = kWave / H;
+    const int64_t nwaves = (T + TW - 1) / TW;
+    for (int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wave < nwaves;
+         wave += (int64_t)gridDim.x * 4) {
+        const int64_t t0 = wave * TW;
+        const int nt = (int)min((int64_t)TW, T - t0);
+        const bool active = lane < nt * H;
+        const int my_k = active ? lane / H : 0;
+        const int h = active ? lane - my_k * H : 0;
+        const int64_t t = t0 + my_k;
+        int32_t w[PLE_MAX_CONTEXT + 1];
+#pragma unroll
+        for (int j = 0; j <= PLE_MAX_CONTEXT; ++j)
+            w[j] = (j <= hp.context_len) ? tok[t - j >= 0 ? t - j : 0] : 0;
+        int r;
+        int64_t a;
+        wave_find_request(qsl, R, t, t0, nt, my_k, lane, r, a);
+        const int32_t id = window_id(hp, w, ctx, r, a, t, h);
+        if (active) ids[t0 * H + lane] = id;
     }
 }
 
@@ -173,9 +228,10 @@ __global__ __launch_bounds__(256) void lookup_kernel(HashParams hp, LookupArgs g
 
 hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int32_t* qsl, int64_t T, int R,
                             const int32_t* ctx, int32_t* ids, hipStream_t s) {
-    const int64_t pairs = T * hp.num_heads;
-    int64_t blocks = (pairs + 255) / 256;
-    if (blocks > 65535 * 16) blocks = 65535 * 16;
+    const int TW = kWave / hp.num_heads;
+    const int64_t waves = (T + TW - 1) / TW;
+    int64_t blocks = (waves + 3) / 4;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
     hipLaunchKernelGGL(ngram_ids_kernel, dim3((unsigned)blocks), dim3(256), 0, s, hp, tok, qsl, T, R, ctx, ids);
     return hipGetLastError();
 }
@@ -190,17 +246,19 @@ hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T,
     return hipGetLastError();
 }
 
-int lookup_tokens_per_block(int64_t T, int H) {
-    int tb = 256 / H;                      // one lane per (token, head) pair in phase 1
-    int64_t target = (T + 1023) / 1024;    // aim for >= 1024 blocks (4 per CU)
-    if (target < tb) tb = (int)(target < 1 ? 1 : target);
-    return tb;
+int lookup_tokens_per_wave(int H, int chunks_per_row) {
+    // about 16 sixteen-byte loads per lane, at most 64 rows (one lane per row for the IDs)
+    const int chunks_per_token = H * chunks_per_row;
+    int tw = (PLE_LOOKUP_LOADS * kWave) / chunks_per_token;
+    if (tw > kWave / H) tw = kWave / H;
+    return tw < 1 ? 1 : tw;
 }
 
 template <int DTYPE, int MODE>
 static hipError_t launch_lookup_t(const HashParams& hp, const LookupArgs& g, hipStream_t s) {
-    const int64_t blocks = (g.num_tokens + g.tokens_per_block - 1) / g.tokens_per_block;
-    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, 16>), dim3((unsigned)blocks), dim3(256), 0, s, hp, g);
+    const int64_t waves = (g.num_tokens + g.tokens_per_wave - 1) / g.tokens_per_wave;
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, PLE_LOOKUP_LOADS>), dim3((unsigned)blocks), dim3(256), 0, s, hp, g);
     return hipGetLastError();
 }
 

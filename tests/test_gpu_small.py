@@ -256,7 +256,9 @@ def _check_kv(got, want, x, w):
 
 
 @pytest.mark.parametrize("M,K,O", [(24, 128, 256), (1, 64, 16), (300, 192, 80), (129, 128, 144),
-                                   (256, 2048, 4096), (1000, 512, 1024)])
+                                   (256, 2048, 4096), (1000, 512, 1024),
+                                   # 256 x 256 tile kernel (>= 256 tiles), ragged in M and O, one K-slice
+                                   (4100, 128, 4112), (4103, 256, 4096), (64, 64, 65536)])
 def test_kv_proj_parity(M, K, O):
     log(f"kv_proj M={M} K={K} O={O}")
     x = wl.normal_bf16((M, K), 100 + M, 0.02)
