@@ -41,8 +41,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=16, help="hash layers rotated over the steps")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=96)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--prefetch-cus", type=int, default=32, help="CUs of the host-table prefetch stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="prefill-8k-bf16-hbm",
+                    choices=["prefill-8k-bf16-hbm", "prefill-16k-fp8-hbm", "prefill-8k-bf16-host"],
+                    help="the default is the benchmark line; the others report the fp8-table and "
+                         "host-resident-table variants")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -57,13 +62,15 @@ def main() -> int:
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cfg = wl.CONFIGS[3]
+    if args.workload == "prefill-8k-bf16-host":
+        return bench_host_table(args)
+    cfg = wl.CONFIGS[3] if args.workload == "prefill-8k-bf16-hbm" else wl.CONFIGS[4]
     L = args.layers
     log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} rows={cfg.num_rows} D={cfg.D} N={cfg.N}")
     b = wl.make_batch(cfg, layers=L)
     log("generating the table on the host")
     t0 = time.time()
-    table_h, _ = wl.make_table(cfg)
+    table_h, scales_h = wl.make_table(cfg)
     log(f"table ready in {time.time() - t0:.1f}s; copying to HBM")
 
     def bf(a):
@@ -72,7 +79,12 @@ def main() -> int:
     def it(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    table = bf(table_h)
+    if cfg.table_dtype == "bf16":
+        table = bf(table_h)
+        tb = ple.Table.from_tensor(table)
+    else:
+        table, scales = it(table_h), it(scales_h)
+        tb = ple.Table.from_tensor(table, scales)
     kv_ws_h = [wl.make_kv_weight(cfg, layer=i) for i in range(4)]
     kv_ws = [bf(w) for w in kv_ws_h]
     conv_w_h = wl.make_conv_weight(cfg)
@@ -80,7 +92,6 @@ def main() -> int:
     hidden_h = wl.make_hidden(cfg)
     hidden = bf(hidden_h)
     toks, qsl = it(b.input_ids), it(b.qsl)
-    tb = ple.Table.from_tensor(table)
     hashes = [ple.HashParams(b.multipliers[l], b.vocab_sizes, b.offsets, heads_per_ngram=cfg.heads_per_ngram,
                              context_len=cfg.context_len, eos_token_id=wl.EOS) for l in range(L)]
     layers = [ple.Layer(hashes[l], tb, kv_ws[l % 4], conv_w, conv_dilation=cfg.conv_dilation, eps=cfg.eps)
@@ -134,13 +145,17 @@ def main() -> int:
         "conv": timed(lambda i: ple.ple_conv(gated, qsl, conv_w, dilation=cfg.conv_dilation, y=out), reps),
     }
     lookup_ms = stage_ms["lookup"]
-    # streaming-copy ceiling: a device-to-device copy of a rows-sized buffer
-    copy_src = torch.empty_like(rows)
-    copy_ms = timed(lambda i: rows.copy_(copy_src), reps)
-    copy_gbps = 2 * rows.numel() * 2 / (copy_ms * 1e-3) / 1e9
+    # streaming-copy ceiling: a device-to-device copy of 1 GiB (four times the
+    # last-level cache, so the copy streams from and to HBM)
+    copy_src = torch.empty((1 << 29,), dtype=torch.bfloat16, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    copy_ms = timed(lambda i: copy_dst.copy_(copy_src), 4)
+    copy_gbps = 2 * copy_src.numel() * 2 / (copy_ms * 1e-3) / 1e9
+    del copy_src, copy_dst
 
     R = b.R
-    lookup_bytes = T * H * D * 2 * 2 + T * 4 + (R + 1) * 4
+    row_read = D * 2 if cfg.table_dtype == "bf16" else D + 4  # fp8 codes + the row's scale
+    lookup_bytes = T * H * (row_read + D * 2) + T * 4 + (R + 1) * 4
     lookup_gbps = lookup_bytes / (lookup_ms * 1e-3) / 1e9
     kv_flops = 2.0 * T * (H * D) * (2 * N)
     kv_tflops = kv_flops / (stage_ms["kv_proj"] * 1e-3) / 1e12
@@ -150,7 +165,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, b, table_h, kv_ws_h[0], conv_w_h, hidden_h, args.cpu_sample_tokens)
+        cpu = cpu_baseline(cfg, b, table_h, scales_h, kv_ws_h[0], conv_w_h, hidden_h, args.cpu_sample_tokens)
 
     line = {
         "metric": METRIC,
@@ -166,13 +181,15 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "requests": R, "heads": H, "orders": [2, 3],
-                   "table_rows": cfg.num_rows, "dim": D, "table_dtype": "bf16", "table_location": "hbm",
+                   "table_rows": cfg.num_rows, "dim": D, "table_dtype": cfg.table_dtype, "table_location": "hbm",
                    "hidden": N, "kv_proj": [H * D, 2 * N], "conv": [cfg.conv_kernel, cfg.conv_dilation],
                    "layers_rotated": L},
         "roofline": {"kernel": "kv_proj (MFMA bf16 GEMM)", "bound": "mfma",
                      "achieved": round(kv_tflops, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(kv_tflops / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None},
-        "lookup": {"kernel": "fused ids+gather", "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
+                     "frac": round(kv_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(cfg.name), "traffic_unit": "bytes per launch"},
+        "lookup": {"kernel": "fused ids+gather" + ("" if cfg.table_dtype == "bf16" else "+fp8 dequant"),
+                   "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
                    "frac_copy_ceiling": round(lookup_gbps / copy_gbps, 4),
                    "tokens_per_s": round(T / (lookup_ms * 1e-3), 1)},
@@ -186,25 +203,178 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(cfg, b, table_h, kvw_h, conv_w_h, hidden_h, n_tokens):
+def recorded_traffic(workload):
+    """HBM bytes per kv_proj launch from the committed counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "kv_proj_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if rec.get("workload") != workload or hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def bench_host_table(args):
+    """Host-resident table: the 8192-token prefill batch over a 67.1M-row
+    (64 GiB) bf16 table in pinned host memory that the lookup kernel reads
+    directly.  Reports the synchronous lookup (host-link GB/s) and, with the
+    next layer's rows prefetched on a CU-masked side stream while the main
+    stream runs a 4096x4096 projection stand-in, the lookup time left exposed
+    per layer."""
+    import numpy as np
+    import torch
+
+    import layer_embedding_lookup_amd as ple
+    import workloads as wl
+
+    dev = "cuda:0"
+    cfg = wl.CONFIGS[5]
+    L = 4
+    T, H, D, N = cfg.T, cfg.H, cfg.D, cfg.N
+    nbytes = cfg.num_rows * D * 2
+    log(f"workload {cfg.name}: allocating {nbytes / 2**30:.1f} GiB of pinned host memory")
+    t0 = time.time()
+    hb = ple.ple_host_alloc(nbytes)
+    log(f"pinned in {time.time() - t0:.1f}s; filling")
+    table_h = hb.numpy(np.uint16, (cfg.num_rows, D))
+    wl.fill_table(cfg, table_h)
+    log(f"table ready after {time.time() - t0:.1f}s")
+    b = wl.make_batch(cfg, layers=L)
+    toks = torch.from_numpy(b.input_ids).to(dev)
+    qsl = torch.from_numpy(b.qsl).to(dev)
+    tb = ple.Table(hb.device, cfg.num_rows, D, ple.PLE_DTYPE_BF16)
+    hashes = [ple.HashParams(b.multipliers[l], b.vocab_sizes, b.offsets, heads_per_ngram=cfg.heads_per_ngram,
+                             context_len=cfg.context_len, eos_token_id=wl.EOS) for l in range(L)]
+    # projection stand-in for the rest of the layer: [8192, 4096] x [4096, 4096]
+    x_std = torch.from_numpy(wl.normal_bf16((T, 4096), 77, 0.02).view(np.int16)).to(dev).view(torch.bfloat16)
+    w_std = torch.from_numpy(wl.normal_bf16((4096, 4096), 78, 0.2).view(np.int16)).to(dev).view(torch.bfloat16)
+    y_std = torch.empty((T, 4096), dtype=torch.bfloat16, device=dev)
+    staging = [torch.empty((T, H * D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    side = ple.ple_stream_create_cu_masked(args.prefetch_cus)
+    # the layer's work runs on a non-blocking stream: the legacy null stream
+    # would serialise with the (blocking) side stream and hide the overlap
+    main = torch.cuda.Stream()
+    torch.cuda.set_stream(main)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    reps = max(2, args.steps // L)
+    try:
+        for _ in range(2):
+            ple.ple_lookup(hashes[0], tb, toks, qsl, rows=staging[0])
+            ple.ple_kv_proj(x_std, w_std, kv=y_std)
+        torch.cuda.synchronize()
+        lookup_ms = timed(lambda i: ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=staging[0]), 2 * L)
+        gemm_ms = timed(lambda i: ple.ple_kv_proj(x_std, w_std, kv=y_std), 2 * L)
+
+        def sync_layer(i):  # lookup on the critical path, then the layer's work
+            ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=staging[0])
+            ple.ple_kv_proj(x_std, w_std, kv=y_std)
+        sync_ms = timed(sync_layer, reps * L)
+
+        def pipelined(n_layers):
+            ready = [torch.cuda.Event() for _ in range(2)]
+            free = [torch.cuda.Event() for _ in range(2)]
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            side.wait_event(e0)
+            ple.ple_lookup(hashes[0], tb, toks, qsl, rows=staging[0], stream=side)
+            ready[0].record(side)
+            for l in range(n_layers):
+                cur, nxt = l % 2, (l + 1) % 2
+                if l + 1 < n_layers:  # prefetch layer l+1 beside layer l
+                    if l >= 1:
+                        side.wait_event(free[nxt])
+                    ple.ple_lookup(hashes[(l + 1) % L], tb, toks, qsl, rows=staging[nxt], stream=side)
+                    ready[nxt].record(side)
+                main.wait_event(ready[cur])
+                ple.ple_kv_proj(x_std, w_std, kv=y_std)   # the layer's work (uses staging[cur] in a real model)
+                free[cur].record(main)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        def staged(n_layers):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(n_layers):
+                ple.ple_kv_proj(x_std, w_std, kv=y_std)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        n_layers = reps * L
+        pipelined(L)
+        pipe_ms = min(pipelined(n_layers) for _ in range(3))
+        staged_ms = min(staged(n_layers) for _ in range(3))
+    finally:
+        torch.cuda.synchronize()
+        ple.ple_stream_destroy(side)
+    rows_bytes = T * H * D * 2
+    line = {
+        "metric": "host-link GB/s and exposed lookup ms per layer, host-resident PLE table, 8k-token prefill",
+        "value": round(rows_bytes / (lookup_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_layers,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "requests": b.R, "heads": H, "table_rows": cfg.num_rows,
+                   "dim": D, "table_location": "pinned host, mapped", "layers": L,
+                   "stand_in": "ple_kv_proj [8192,4096]x[4096,4096]", "prefetch_cus": args.prefetch_cus},
+        "lookup_ms_sync": round(lookup_ms, 4),
+        "host_link_GBps": round(rows_bytes / (lookup_ms * 1e-3) / 1e9, 2),
+        "stand_in_ms": round(gemm_ms, 4),
+        "sync_ms_per_layer": round(sync_ms, 4),
+        "pipelined_ms_per_layer": round(pipe_ms / n_layers, 4),
+        "staged_ms_per_layer": round(staged_ms / n_layers, 4),
+        "exposed_lookup_ms_per_layer": round((pipe_ms - staged_ms) / n_layers, 4),
+        "exposed_floor_ms_per_layer": round(max(0.0, lookup_ms - gemm_ms), 4),
+    }
+    print(json.dumps(line), flush=True)
+    hb.close()
+    return 0
+
+
+def cpu_baseline(cfg, b, table_h, scales_h, kvw_h, conv_w_h, hidden_h, n_tokens):
     """The oracle, single-threaded, on a bounded sample: the first n_tokens of
-    request 0 (a prefix chunk) through the whole path."""
+    the batch (whole requests, the last one cut to a prefix chunk; by causality
+    their outputs equal the full batch's) through the whole path."""
     import numpy as np
 
     import oracle
     import workloads as wl
 
-    n = int(min(n_tokens, int(b.qsl[1])))
-    log(f"cpu baseline: oracle on the first {n} tokens of request 0 (whole path)")
-    ids_args = dict(input_ids=b.input_ids[:n], qsl=np.asarray([0, n], np.int32), multipliers=b.multipliers[0],
+    n = int(min(n_tokens, cfg.T))
+    q = b.qsl.astype(np.int64)
+    R = int(np.searchsorted(q, n, side="left"))  # requests 0..R-1 cover [0, n)
+    qsl = np.minimum(q[:R + 1], n).astype(np.int32)
+    qsl[-1] = n
+    log(f"cpu baseline: oracle on the first {n} tokens ({R} requests), whole path")
+    ids_args = dict(input_ids=b.input_ids[:n], qsl=qsl, multipliers=b.multipliers[0],
                     vocab_sizes=b.vocab_sizes, offsets=b.offsets, context_len=cfg.context_len,
                     heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS)
     t0 = time.perf_counter()
-    oracle.prefill(ids_args, table_h, None, hidden_h[:n], kvw_h, conv_w_h, cfg.conv_dilation,
-                   qsl=np.asarray([0, n], np.int32), eps=cfg.eps)
+    oracle.prefill(ids_args, table_h, scales_h, hidden_h[:n], kvw_h, conv_w_h, cfg.conv_dilation, qsl=qsl,
+                   eps=cfg.eps)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} tokens of request 0 of the {cfg.name} batch, whole path "
+            "sample": f"first {n} tokens ({R} requests) of the {cfg.name} batch, whole path "
                       f"(ids, gather, kv_proj, gate, conv), single-threaded C, {dt:.1f} s"}
 
 

@@ -230,7 +230,9 @@ int ple_host_free(void* host);
  * A stream restricted to the first num_cus compute units of the current
  * device, for running the prefetch beside the main stream ([P2] 实现拆解
  * item 4 launches the lookup on a side stream with half the grid).  Default
- * priority.  ple_stream_destroy releases it.
+ * priority.  Like any stream created without the non-blocking flag it
+ * synchronises with the legacy null stream: run the overlapped main work on a
+ * non-blocking stream.  ple_stream_destroy releases it.
  */
 int ple_stream_create_cu_masked(int32_t num_cus, void** stream);
 int ple_stream_destroy(void* stream);

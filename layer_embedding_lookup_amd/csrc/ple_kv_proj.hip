@@ -178,39 +178,59 @@ __global__ __launch_bounds__(256) void kv_proj_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Large-problem kernel: 256 x 256 x 64 block tile, 4 waves of 128 x 128.
+// Large-problem kernel: 256 x 256 block tile, 8 waves (two per SIMD) of
+// 128 x 64, K-slices of 32 in a ring of 4 LDS stages.
 //
 // Operands go global -> LDS with the gfx950 direct-to-LDS 16-byte loads
-// (global_load_lds_dwordx4): no register staging, and the copy of the next
-// K-slice runs while the MFMAs consume the current one (two LDS stages).  One
-// wave instruction fills 1 KiB of LDS = 8 rows x 8 16-byte chunks; each lane
-// picks the global chunk so that LDS holds chunk (row, kc) at position
-// row*8 + (kc ^ ((row >> 1) & 7)).  An MFMA fragment read takes one k-chunk
-// of 32 consecutive rows; the LDS serves 16 lanes (256 bytes, 64 banks) per
-// cycle, and with this swizzle any 16 consecutive rows land on 16 distinct
-// 16-byte bank groups (row parity picks the half, (row >> 1) & 7 the group).  The MFMA operands are swapped (W fragment first)
-// so each lane's accumulators are 4 consecutive output features of one token,
-// which the epilogue writes to LDS as 8-byte pairs before the coalesced
-// 16-byte global stores.
+// (global_load_lds_dwordx4): no register staging.  The copies run three
+// slices ahead of the MFMAs (about three slices of compute to arrive from L2,
+// the last-level cache or HBM).  Each thread waits only for its own copies of
+// the slice it is about to use (vmcnt lets the later slices stay in flight),
+// then one barrier makes everyone's copies visible and frees the stage the
+// next copy overwrites.  With two waves per SIMD, one wave's MFMAs cover the
+// other's LDS fragment reads.
+//
+// LDS layout of a stage: rows of 32 bf16 = 4 chunks of 16 bytes, chunk
+// (row, kc) at position row*4 + (kc ^ ((row >> 2) & 3)).  An MFMA fragment
+// read takes one k-chunk of 32 consecutive rows; the LDS serves 16 lanes
+// (256 bytes, 64 banks) per cycle, and any 16 consecutive rows land on 16
+// distinct 16-byte bank groups.  One wave copy instruction fills 1 KiB =
+// 16 rows x 4 chunks, each lane fetching the global chunk that belongs at its
+// position.  The MFMA operands are swapped (W fragment first) so each lane's
+// accumulators are 4 consecutive output features of one token, which the
+// epilogue writes to LDS as 8-byte pairs before coalesced 16-byte stores.
 // ---------------------------------------------------------------------------
 constexpr int kBigTile = 256;
-constexpr int kBigStageBytes = 2 * kBigTile * kBK * 2;          // A + B slices: 64 KiB
-constexpr int kBigOutRow = kBigTile + 8;                         // epilogue row (elements)
-constexpr int kBigLdsBytes = (2 * kBigStageBytes > kBigTile * kBigOutRow * 2) ? 2 * kBigStageBytes
-                                                                              : kBigTile * kBigOutRow * 2;
+constexpr int kBigThreads = 512;
+constexpr int kBBK = 32;
+constexpr int kNStage = 4;
+constexpr int kBigStageBytes = 2 * kBigTile * kBBK * 2;  // x + W slices: 32 KiB
+constexpr int kBigOutRow = kBigTile + 8;                 // epilogue row (elements)
+constexpr int kBigLdsBytes = (kNStage * kBigStageBytes > kBigTile * kBigOutRow * 2) ? kNStage * kBigStageBytes
+                                                                                    : kBigTile * kBigOutRow * 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ ((row >> 1) & 7)); }
+__device__ __forceinline__ int swz4(int row, int kc) { return row * 4 + (kc ^ ((row >> 2) & 3)); }
 
-__global__ __launch_bounds__(256, 1) void kv_proj_big_kernel(const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ w, int M, int K, int O,
-                                                             uint16_t* __restrict__ out) {
+// Wait until at most n of this wave's vector-memory operations (the later
+// slices' copies) are outstanding and all its LDS reads are complete, then
+// join the workgroup barrier.  __syncthreads() would wait for every copy in
+// flight (its release fence counts direct-to-LDS copies as pending LDS
+// writes), which would serialise the copy pipeline.  The "memory" clobber
+// keeps the compiler from moving LDS or global accesses across the barrier.
+#define PLE_STR2(x) #x
+#define PLE_STR(x) PLE_STR2(x)
+#define PLE_WAIT_VM_BARRIER(n) asm volatile("s_waitcnt vmcnt(" PLE_STR(n) ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+__global__ __launch_bounds__(kBigThreads, 1) void kv_proj_big_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ w, int M, int K,
+                                                                     int O, uint16_t* __restrict__ out) {
     extern __shared__ __align__(16) char lds_raw[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 tokens x 64 features each
 
     const int tiles_m = (M + kBigTile - 1) / kBigTile;
     const int tiles_n = (O + kBigTile - 1) / kBigTile;
@@ -218,94 +238,96 @@ __global__ __launch_bounds__(256, 1) void kv_proj_big_kernel(const uint16_t* __r
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * kBigTile, n0 = tn * kBigTile;
 
-    // per-lane source rows for the 8 load instructions of each operand:
-    // instruction i of wave `wave` fills rows g*8 .. g*8+7 with g = i*4 + wave
-    // lane L writes LDS position group*64 + L = row*8 + (kc ^ ((row >> 1) & 7)),
-    // row = group*8 + L/8: it fetches global chunk kc = (L & 7) ^ ((row >> 1) & 7)
-    const int lrow = lane >> 3;  // row within the 8-row group
-    const uint16_t* asrc[8];
-    const uint16_t* bsrc[8];
+    // copy instruction i (0..1) of wave `wave` fills rows g*16 .. g*16+15 of
+    // each operand, g = i*8 + wave; lane L lands at position g*64 + L:
+    // row = g*16 + L/4, chunk kc = (L & 3) ^ ((L >> 4) & 3)
+    const int lkc = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint16_t* asrc[2];
+    const uint16_t* bsrc[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = (i * 4 + wave) * 8 + lrow;
-        const int lkc = (lane & 7) ^ ((row >> 1) & 7);
+    for (int i = 0; i < 2; ++i) {
+        const int row = (i * 8 + wave) * 16 + (lane >> 2);
         asrc[i] = x + (int64_t)min(m0 + row, M - 1) * K + lkc * 8;
         bsrc[i] = w + (int64_t)min(n0 + row, O - 1) * K + lkc * 8;
     }
-    auto issue_slice = [&](int kt, int stage) {
-        char* base = lds_raw + stage * kBigStageBytes;
+    auto issue_slice = [&](int kt) {
+        char* base = lds_raw + (kt % kNStage) * kBigStageBytes;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int g = i * 4 + wave;
-            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * kBK), (lds_ptr_t)(base + g * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + kt * kBK),
-                                             (lds_ptr_t)(base + kBigTile * kBK * 2 + g * 1024), 16, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+            const int g = i * 8 + wave;
+            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * kBBK), (lds_ptr_t)(base + g * 1024), 16, 0,
+                                             0);
+            __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + kt * kBBK),
+                                             (lds_ptr_t)(base + kBigTile * kBBK * 2 + g * 1024), 16, 0, 0);
         }
     };
 
-    f32x16 acc[4][4];  // [W sub-tile j][x sub-tile i]
+    f32x16 acc[2][4];  // [W sub-tile j][x sub-tile i]
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
-    const int nk = K / kBK;
-    issue_slice(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+    // per thread and slice: 2 x + 2 W copy instructions (the waits below count 4)
+    const int nk = K / kBBK;
+#pragma unroll
+    for (int p = 0; p < kNStage - 1; ++p)
+        if (p < nk) issue_slice(p);
 
     const int frow = lane & 31;
     const int fk = lane >> 5;
     for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < nk) issue_slice(kt + 1, stage ^ 1);
-        const u32x4* As = (const u32x4*)(lds_raw + stage * kBigStageBytes);
-        const u32x4* Bs = As + kBigTile * 8;
+        // slices <= kt complete: the copies of up to two later slices may remain in flight;
+        // after the barrier stage (kt-1) % 4, read in the previous iteration, is free
+        const int ahead = min(nk - 1 - kt, kNStage - 2);
+        if (ahead >= 2)
+            PLE_WAIT_VM_BARRIER(8);
+        else if (ahead == 1)
+            PLE_WAIT_VM_BARRIER(4);
+        else
+            PLE_WAIT_VM_BARRIER(0);
+        if (kt + kNStage - 1 < nk) issue_slice(kt + kNStage - 1);
+
+        const u32x4* As = (const u32x4*)(lds_raw + (kt % kNStage) * kBigStageBytes);
+        const u32x4* Bs = As + kBigTile * 4;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2; ++kk) {
             const int kc = kk * 2 + fk;
-            bf16x8 af[4], bfr[4];
+            bf16x8 af[4], bfr[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 128 + i * 32 + frow;
-                af[i] = __builtin_bit_cast(bf16x8, As[swz(row, kc)]);
-            }
+            for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, As[swz4(wm * 128 + i * 32 + frow, kc)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = wn * 128 + j * 32 + frow;
-                bfr[j] = __builtin_bit_cast(bf16x8, Bs[swz(row, kc)]);
-            }
+            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, Bs[swz4(wn * 64 + j * 32 + frow, kc)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // this lane's copies of the next slice have landed
-        __syncthreads();                     // ... and everyone's; the current stage is free again
     }
+    __syncthreads();  // all reads of the last stage are done before the epilogue reuses LDS
 
-    // epilogue: acc[j][i][e] is feature n0 + wn*128 + j*32 + 8*(e/4) + 4*(lane/32) + e%4
+    // epilogue: acc[j][i][e] is feature n0 + wn*64 + j*32 + 8*(e/4) + 4*(lane/32) + e%4
     // of token m0 + wm*128 + i*32 + lane%32
     uint16_t* Cs = (uint16_t*)lds_raw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int m = wm * 128 + i * 32 + frow;
-                const int o = wn * 128 + j * 32 + 8 * g + 4 * fk;
+                const int o = wn * 64 + j * 32 + 8 * g + 4 * fk;
                 const uint32_t lo = pack_bf16x2(acc[j][i][4 * g], acc[j][i][4 * g + 1]);
                 const uint32_t hi = pack_bf16x2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
                 *(uint2*)(Cs + m * kBigOutRow + o) = make_uint2(lo, hi);
             }
     __syncthreads();
 #pragma unroll 4
-    for (int c = tid; c < kBigTile * kBigTile / 8; c += 256) {
-        const int row = c >> 5;           // 32 chunks of 8 features per row
+    for (int c = tid; c < kBigTile * kBigTile / 8; c += kBigThreads) {
+        const int row = c >> 5;  // 32 chunks of 8 features per row
         const int col = (c & 31) * 8;
         const int gr = m0 + row, gc = n0 + col;
         if (gr < M && gc < O) *(u32x4*)(out + (int64_t)gr * O + gc) = *(const u32x4*)(Cs + row * kBigOutRow + col);
@@ -318,7 +340,7 @@ static hipError_t launch_kv_proj_big(const uint16_t* x, const uint16_t* w, int64
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kBigLdsBytes);
     if (attr != hipSuccess) return attr;
     const int tiles = (int)((M + kBigTile - 1) / kBigTile) * ((O + kBigTile - 1) / kBigTile);
-    hipLaunchKernelGGL(kv_proj_big_kernel, dim3(tiles), dim3(256), kBigLdsBytes, s, x, w, (int)M, K, O, kv);
+    hipLaunchKernelGGL(kv_proj_big_kernel, dim3(tiles), dim3(kBigThreads), kBigLdsBytes, s, x, w, (int)M, K, O, kv);
     return hipGetLastError();
 }
 

@@ -165,18 +165,24 @@ def prefill(batch_ids_args: dict, table, scales, hidden, kv_weight, conv_weight,
             qsl, eps=1e-6, conv_state=None, tokens=None):
     """Whole path: ids -> rows -> kv -> gate -> conv.
 
-    ``tokens`` (optional, sorted) restricts kv_proj to the listed tokens and the
-    conv taps they need; outputs at other tokens are then meaningless, and the
-    caller compares only the listed ones.  Returns a dict of every stage.
+    ``tokens`` (optional, sorted) restricts the row gather and kv_proj to the
+    listed tokens and the conv taps they need; outputs at other tokens are then
+    meaningless, and the caller compares only the listed ones.  Returns a dict
+    of every stage.
     """
     ids = ngram_ids(**batch_ids_args)
     T, H = ids.shape
-    rows = gather_bf16(table, ids) if scales is None else gather_fp8(table, scales, ids)
-    rows = rows.reshape(T, -1)
+
+    def gather(sel):
+        return gather_bf16(table, sel) if scales is None else gather_fp8(table, scales, sel)
+
     if tokens is None:
+        rows = gather(ids).reshape(T, -1)
         kv = kv_proj(rows, kv_weight)
     else:
         need = conv_taps(tokens, qsl, conv_weight.shape[1], dilation)
+        rows = np.zeros((T, H * table.shape[1]), dtype=np.uint16)
+        rows[need] = gather(ids[need]).reshape(len(need), -1)
         kv = np.zeros((T, kv_weight.shape[0]), dtype=np.uint16)
         kv[need] = kv_proj(rows[need], kv_weight)
     out, g = gate(hidden, kv, eps)

@@ -8,6 +8,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------ */
@@ -173,13 +174,26 @@ void orc_gather_fp8(const uint8_t* codes, const float* scales, int32_t dim, cons
 /* ------------------------------------------------------------------------ */
 
 void orc_kv_proj(const uint16_t* x, const uint16_t* w, int64_t T, int32_t K, int32_t O, uint16_t* kv) {
-    for (int64_t t = 0; t < T; ++t)
+    /* the operands widened to double once (exact), then plain dot products */
+    double* wd = (double*)malloc(sizeof(double) * (size_t)O * (size_t)K);
+    double* xd = (double*)malloc(sizeof(double) * (size_t)K);
+    if (wd == NULL || xd == NULL) {
+        free(wd);
+        free(xd);
+        return;
+    }
+    for (int64_t i = 0; i < (int64_t)O * K; ++i) wd[i] = orc_bf16_value(w[i]);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) xd[k] = orc_bf16_value(x[t * K + k]);
         for (int32_t o = 0; o < O; ++o) {
+            const double* wr = wd + (int64_t)o * K;
             double acc = 0.0;
-            for (int32_t k = 0; k < K; ++k)
-                acc += orc_bf16_value(x[t * K + k]) * orc_bf16_value(w[(int64_t)o * K + k]);
+            for (int32_t k = 0; k < K; ++k) acc += xd[k] * wr[k];
             kv[t * O + o] = orc_bf16_from_double(acc);
         }
+    }
+    free(wd);
+    free(xd);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -1,0 +1,161 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the
+benchmark times.  IDs and gathered rows (bf16 copy, fp8 dequant) are compared
+bit-exactly on every token; kv_proj, gate and conv outputs are compared on a
+deterministic token sample the oracle computes one by one (the first and last
+tokens of every request plus seeded random tokens, with their conv taps; the
+sizes are in SAMPLE).
+
+Workloads: the 8192-token prefill over an 8.39M-row bf16 table in HBM, the
+16384-token prefill over a 33.6M-row fp8 e4m3fn table with per-row scales,
+and the 8192-token prefill over a 67.1M-row (64 GiB) bf16 table in pinned
+host memory read directly by the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import layer_embedding_lookup_amd as ple
+import oracle
+import workloads as wl
+from gpu_util import DEV, bf16_f64, dev, dev_bf16, hash_params, host_bits, log, oracle_ids
+
+pytestmark = pytest.mark.gpu
+
+OUT_ABS_TOL = 2e-2
+
+
+def _sample_tokens(qsl, T, first, last, rand, seed=0):
+    q = np.asarray(qsl, dtype=np.int64)
+    pick = set()
+    for r in range(len(q) - 1):
+        a, b = int(q[r]), int(q[r + 1])
+        pick.update(range(a, min(b, a + first)))
+        pick.update(range(max(a, b - last), b))
+    pick.update(np.random.default_rng(seed).integers(0, T, rand).tolist())
+    return np.asarray(sorted(pick), dtype=np.int64)
+
+
+# the oracle's double-precision kv_proj costs ~K*2N multiply-adds per sampled token
+SAMPLE = {3: (16, 4, 16), 4: (4, 2, 8), 5: (16, 4, 16)}
+
+
+def _check_chain(cfg, b, table_h, scales_h, layer, hidden_h, kvw_h, cw_h, got_out):
+    tokens = _sample_tokens(b.qsl, cfg.T, *SAMPLE[cfg.idx])
+    log(f"oracle chain on {len(tokens)} sampled tokens")
+    ids_args = dict(input_ids=b.input_ids, qsl=b.qsl, multipliers=b.multipliers[layer], vocab_sizes=b.vocab_sizes,
+                    offsets=b.offsets, context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram,
+                    eos_token_id=wl.EOS, ngram_context=b.ngram_context)
+    ref = oracle.prefill(ids_args, table_h, scales_h, hidden_h, kvw_h, cw_h, cfg.conv_dilation, qsl=b.qsl,
+                         eps=cfg.eps, conv_state=b.conv_state, tokens=tokens)
+    diff = np.abs(bf16_f64(got_out[tokens]) - bf16_f64(ref["y"][tokens]))
+    log(f"max |out - oracle| on the sample: {diff.max():.4g}")
+    assert diff.max() <= OUT_ABS_TOL
+
+
+def _prefill_full(cfg, table_tensor, scales_tensor, table_h, scales_h, layer=1):
+    b = wl.make_batch(cfg, layers=2)
+    log(f"{cfg.name}: T={cfg.T} R={b.R} H={cfg.H} rows={cfg.num_rows}")
+    tb = ple.Table.from_tensor(table_tensor, scales_tensor)
+    toks, qsl = dev(b.input_ids), dev(b.qsl)
+    hp = hash_params(b, layer)
+    # ids and rows, every token
+    ids_out = torch.empty((cfg.T, cfg.H), dtype=torch.int32, device=DEV)
+    rows = ple.ple_lookup(hp, tb, toks, qsl, ids_out=ids_out)
+    want_ids = oracle_ids(b, layer)
+    np.testing.assert_array_equal(ids_out.cpu().numpy(), want_ids)
+    if scales_h is None:
+        want_rows = table_h[want_ids.reshape(-1)].reshape(cfg.T, -1)
+    else:
+        want_rows = oracle.gather_fp8(table_h, scales_h, want_ids).reshape(cfg.T, -1)
+    np.testing.assert_array_equal(host_bits(rows), want_rows)
+    log("ids and rows bit-exact on every token")
+    # whole path through the fused entry point
+    kvw_h = wl.make_kv_weight(cfg, layer=layer)
+    cw_h = wl.make_conv_weight(cfg)
+    hidden_h = wl.make_hidden(cfg)
+    L = ple.Layer(hp, tb, dev_bf16(kvw_h), dev_bf16(cw_h), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    out = ple.ple_prefill_fused(L, toks, qsl, dev_bf16(hidden_h))
+    _check_chain(cfg, b, table_h, scales_h, layer, hidden_h, kvw_h, cw_h, host_bits(out))
+
+
+def test_prefill_8k_bf16_hbm_full():
+    cfg = wl.CONFIGS[3]
+    log("generating the 8.6 GB table")
+    table_h, _ = wl.make_table(cfg)
+    _prefill_full(cfg, dev_bf16(table_h), None, table_h, None)
+
+
+def test_prefill_16k_fp8_hbm_full():
+    cfg = wl.CONFIGS[4]
+    log("generating the 17.2 GB fp8 table")
+    q_h, s_h = wl.make_table(cfg)
+    _prefill_full(cfg, dev(q_h), dev(s_h), q_h, s_h)
+
+
+def test_prefill_8k_host_table_full():
+    cfg = wl.CONFIGS[5]
+    nbytes = cfg.num_rows * cfg.D * 2
+    log(f"allocating {nbytes / 2**30:.1f} GiB of pinned host memory")
+    hb = ple.ple_host_alloc(nbytes)
+    try:
+        table_h = hb.numpy(np.uint16, (cfg.num_rows, cfg.D))
+        log("filling the host table")
+        wl.fill_table(cfg, table_h)
+        b = wl.make_batch(cfg, layers=2)
+        toks, qsl = dev(b.input_ids), dev(b.qsl)
+        tb_host = ple.Table(hb.device, cfg.num_rows, cfg.D, ple.PLE_DTYPE_BF16)
+        for layer in range(2):
+            hp = hash_params(b, layer)
+            ids = ple.ple_ngram_ids(hp, toks, qsl)
+            rows = ple.ple_lookup(hp, tb_host, toks, qsl)
+            want_ids = oracle_ids(b, layer)
+            np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+            np.testing.assert_array_equal(host_bits(rows), table_h[want_ids.reshape(-1)].reshape(cfg.T, -1))
+            log(f"layer {layer}: host-mapped rows bit-exact on every token")
+        # prefetch on a CU-masked side stream, then the rest of the path on the main stream
+        layer = 1
+        hp = hash_params(b, layer)
+        kvw_h = wl.make_kv_weight(cfg, layer=layer)
+        cw_h = wl.make_conv_weight(cfg)
+        hidden_h = wl.make_hidden(cfg)
+        L = ple.Layer(hp, tb_host, dev_bf16(kvw_h), dev_bf16(cw_h), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+        side = ple.ple_stream_create_cu_masked(64)
+        try:
+            staging = torch.empty((cfg.T, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+            ev0 = torch.cuda.Event()
+            ev0.record()
+            side.wait_event(ev0)
+            ple.ple_prefetch(L, toks, qsl, staging, stream=side)
+            ev = torch.cuda.Event()
+            ev.record(side)
+            torch.cuda.current_stream().wait_event(ev)
+            out = ple.ple_prefill_fused(L, toks, qsl, dev_bf16(hidden_h), prefetched_rows=staging)
+            torch.cuda.synchronize()
+        finally:
+            ple.ple_stream_destroy(side)
+        _check_chain(cfg, b, table_h, None, layer, hidden_h, kvw_h, cw_h, host_bits(out))
+    finally:
+        torch.cuda.synchronize()
+        hb.close()
+
+
+def test_decode_256_full_chain():
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    table_h, _ = wl.make_table(cfg)
+    tb = ple.Table.from_tensor(dev_bf16(table_h))
+    kvw_h, cw_h, hidden_h = wl.make_kv_weight(cfg), wl.make_conv_weight(cfg), wl.make_hidden(cfg)
+    hp = hash_params(b)
+    L = ple.Layer(hp, tb, dev_bf16(kvw_h), dev_bf16(cw_h), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    st_out = torch.empty((b.R, cfg.S, cfg.N), dtype=torch.bfloat16, device=DEV)
+    ctx_out = torch.empty((b.R, cfg.context_len), dtype=torch.int32, device=DEV)
+    out = ple.ple_prefill_fused(L, dev(b.input_ids), dev(b.qsl), dev_bf16(hidden_h),
+                                ngram_context=dev(b.ngram_context), ngram_context_out=ctx_out,
+                                conv_state=dev_bf16(b.conv_state), conv_state_out=st_out)
+    ids_args = dict(input_ids=b.input_ids, qsl=b.qsl, multipliers=b.multipliers[0], vocab_sizes=b.vocab_sizes,
+                    offsets=b.offsets, context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram,
+                    eos_token_id=wl.EOS, ngram_context=b.ngram_context)
+    ref = oracle.prefill(ids_args, table_h, None, hidden_h, kvw_h, cw_h, cfg.conv_dilation, qsl=b.qsl,
+                         eps=cfg.eps, conv_state=b.conv_state)
+    assert np.abs(bf16_f64(host_bits(out)) - bf16_f64(ref["y"])).max() <= OUT_ABS_TOL
+    _, want_ctx = oracle_ids(b, want_context_out=True)
+    np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
