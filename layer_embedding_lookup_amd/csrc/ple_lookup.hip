@@ -31,6 +31,9 @@
 #ifndef PLE_LOOKUP_NT_STORE
 #define PLE_LOOKUP_NT_STORE 0
 #endif
+#ifndef PLE_LOOKUP_BLOCK
+#define PLE_LOOKUP_BLOCK 256  // threads per block; waves are independent
+#endif
 
 namespace ple {
 
@@ -116,9 +119,9 @@ __device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
 // wave computes its IDs and streams its rows on its own.  MODE_HASH computes
 // the IDs, MODE_IDS reads (and clamps) caller IDs.
 template <int DTYPE, int MODE, int UNROLL>
-__global__ __launch_bounds__(256) void lookup_kernel(HashParams hp, LookupArgs g) {
+__global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp, LookupArgs g) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t wave = (int64_t)blockIdx.x * (PLE_LOOKUP_BLOCK / kWave) + (threadIdx.x >> 6);
     const int TW = g.tokens_per_wave;
     const int64_t t0 = wave * TW;
     if (t0 >= g.num_tokens) return;  // whole wave
@@ -256,9 +259,11 @@ int lookup_tokens_per_wave(int H, int chunks_per_row) {
 
 template <int DTYPE, int MODE>
 static hipError_t launch_lookup_t(const HashParams& hp, const LookupArgs& g, hipStream_t s) {
+    constexpr int WPB = PLE_LOOKUP_BLOCK / kWave;  // waves per block
     const int64_t waves = (g.num_tokens + g.tokens_per_wave - 1) / g.tokens_per_wave;
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, PLE_LOOKUP_LOADS>), dim3((unsigned)blocks), dim3(256), 0, s, hp, g);
+    const int64_t blocks = (waves + WPB - 1) / WPB;
+    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, PLE_LOOKUP_LOADS>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK),
+                       0, s, hp, g);
     return hipGetLastError();
 }
 
