@@ -257,15 +257,22 @@ def _check_kv(got, want, x, w):
 
 @pytest.mark.parametrize("M,K,O", [(24, 128, 256), (1, 64, 16), (300, 192, 80), (129, 128, 144),
                                    (256, 2048, 4096), (1000, 512, 1024),
-                                   # 256 x 256 tile kernel (>= 256 tiles), ragged in M and O, one K-slice
-                                   (4100, 128, 4112), (4103, 256, 4096), (64, 64, 65536)])
+                                   # 256 x 256 tile kernel (>= 256 tiles): 1 to 5 K-slices of 64,
+                                   # ragged in M and in O
+                                   (4100, 128, 4112), (4103, 256, 4096), (64, 64, 65536), (2048, 192, 8192),
+                                   (2100, 320, 8208)])
 def test_kv_proj_parity(M, K, O):
     log(f"kv_proj M={M} K={K} O={O}")
     x = wl.normal_bf16((M, K), 100 + M, 0.02)
     w = wl.normal_bf16((O, K), 200 + O, 12.5 / np.sqrt(K))
-    want = oracle.kv_proj(x, w)
     got = host_bits(ple.ple_kv_proj(dev_bf16(x), dev_bf16(w)))
-    _check_kv(got, want, x, w)
+    if M * O * K > 4e9:
+        # the oracle takes the first and last rows (ragged tile edge) and a seeded sample
+        rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(M - 40, M),
+                                         np.random.default_rng(M).integers(0, M, 40)]))
+        _check_kv(got[rows], oracle.kv_proj(x[rows], w), x[rows], w)
+    else:
+        _check_kv(got, oracle.kv_proj(x, w), x, w)
 
 
 def test_kv_proj_sampled_rows_at_prefill_shape():
