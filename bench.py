@@ -145,6 +145,16 @@ def main() -> int:
         "conv": timed(lambda i: ple.ple_conv(gated, qsl, conv_w, dilation=cfg.conv_dilation, y=out), reps),
     }
     lookup_ms = stage_ms["lookup"]
+    # Reference points for the lookup, same bytes and buffers: the row output
+    # written alone (torch fill, no reads), and, for a bf16 table, torch's own
+    # embedding gather on the same IDs (an index_select into the same output).
+    write_only_ms = timed(lambda i: rows.fill_(1.0), 4 * L)
+    torch_gather_ms = None
+    if cfg.table_dtype == "bf16":
+        ids_l = [ple.ple_ngram_ids(hashes[l], toks, qsl).view(-1).long() for l in range(L)]
+        rows_flat = rows.view(T * H, D)
+        torch_gather_ms = timed(lambda i: torch.index_select(table, 0, ids_l[i % L], out=rows_flat), 4 * L)
+        del ids_l
     # streaming-copy ceiling: a device-to-device copy of 1 GiB (four times the
     # last-level cache, so the copy streams from and to HBM)
     copy_src = torch.empty((1 << 29,), dtype=torch.bfloat16, device=dev)
@@ -192,7 +202,9 @@ def main() -> int:
                    "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
                    "frac_copy_ceiling": round(lookup_gbps / copy_gbps, 4),
-                   "tokens_per_s": round(T / (lookup_ms * 1e-3), 1)},
+                   "tokens_per_s": round(T / (lookup_ms * 1e-3), 1),
+                   "write_only_ms": round(write_only_ms, 5),
+                   "torch_index_select_ms": None if torch_gather_ms is None else round(torch_gather_ms, 5)},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_GBps": {"gate": round(gate_bytes / (stage_ms["gate"] * 1e-3) / 1e9, 1),
                         "conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)},
