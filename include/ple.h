@@ -63,7 +63,14 @@ extern "C" {
 #define PLE_ERR_WORKSPACE 4
 
 #define PLE_DTYPE_BF16 0
-#define PLE_DTYPE_FP8_E4M3 1 /* OCP float8 e4m3fn: bias 7, max 448, NaN 0x7F/0xFF */
+#define PLE_DTYPE_FP8_E4M3 1 /* OCP float8 e4m3fn: bias 7, max 448, NaN 0x7F/0xFF; one fp32 scale per row */
+/* float8 e4m3fn codes with one fp32 scale for the whole table ([P4] review
+ * thread: an FP8 PLE table with one global weight_scale) */
+#define PLE_DTYPE_FP8_E4M3_GLOBAL 2
+/* NVFP4 ([P4] walkthrough: NVFP4 embedding support): 4-bit e2m1 codes, two
+ * per byte (element 2i in the low nibble of byte i), an e4m3fn scale per
+ * 16-element block and one fp32 scale for the whole table */
+#define PLE_DTYPE_NVFP4 3
 
 #define PLE_MAX_HEADS 32
 #define PLE_MAX_CONTEXT 7
@@ -89,13 +96,23 @@ typedef struct ple_hash_desc {
     const int64_t* offsets;     /* host [H]; >= 0; offsets[h] + V_h <= table rows and < 2^31 */
 } ple_hash_desc;
 
-/* An embedding table of one layer ([P1] 关键源码片段; [P4] FP8 tables). */
+/*
+ * An embedding table of one layer ([P1] 关键源码片段; [P4] FP8 and NVFP4
+ * tables).  Every decoded element is one fp32 value rounded once to bf16
+ * (nearest, ties to even):
+ *   BF16:             the stored bits
+ *   FP8_E4M3:         float(e4m3fn(code)) * row_scales[row]        (one fp32 multiply)
+ *   FP8_E4M3_GLOBAL:  float(e4m3fn(code)) * row_scales[0]          (one fp32 multiply)
+ *   NVFP4:            (e2m1(code) * e4m3fn(block scale)) * row_scales[0]
+ *                     (the first product is exact in fp32; one fp32 multiply)
+ */
 typedef struct ple_table_desc {
-    const void* table;        /* device (or mapped host) [num_rows][dim] elements of dtype */
+    const void* table;        /* device (or mapped host) [num_rows][row bytes]: D bf16, D fp8 codes or D/2 bytes of fp4 codes */
     int64_t num_rows;         /* 1 .. 2^31 */
-    int32_t dim;              /* D; D*elem_size a multiple of 16 bytes, D <= 8192 */
-    int32_t dtype;            /* PLE_DTYPE_BF16 | PLE_DTYPE_FP8_E4M3 */
-    const float* row_scales;  /* fp8 only: device (or mapped host) [num_rows]; NULL for bf16 */
+    int32_t dim;              /* D <= 8192; row bytes a multiple of 16 (NVFP4: D a multiple of 32) */
+    int32_t dtype;            /* PLE_DTYPE_* */
+    const float* row_scales;  /* FP8_E4M3: [num_rows]; FP8_E4M3_GLOBAL and NVFP4: [1]; NULL for BF16 */
+    const uint8_t* block_scales; /* NVFP4: e4m3fn codes [num_rows][D/16]; NULL otherwise */
 } ple_table_desc;
 
 /*
@@ -141,10 +158,10 @@ typedef struct ple_layer_desc {
 int ple_ngram_ids(const ple_hash_desc* hash, const ple_batch_desc* batch, int32_t* ids, void* stream);
 
 /*
- * Row gather ([P1] 关键源码片段, the embedding lookup; [P4] FP8 tables):
- *   rows[t][h*D + c] = table[ids[t][h]][c]                         (bf16, bit copy)
- *   rows[t][h*D + c] = bf16(float(e4m3fn(q[id][c])) * scale[id])   (fp8: one fp32
- *                      multiply, round-to-nearest-even; NaN codes give 0x7FC0)
+ * Row gather ([P1] 关键源码片段, the embedding lookup; [P4] FP8 and NVFP4 tables):
+ *   rows[t][h*D + c] = decoded element c of table row ids[t][h], as listed at
+ *   ple_table_desc (bf16: bit copy; quantised formats: one fp32 value rounded
+ *   to nearest even; NaN codes or NaN scales give 0x7FC0)
  * ids: device int32 [T][H], every id in [0, num_rows) (ids outside are clamped
  * into range, so a bad id never reads outside the table).  rows: device bf16
  * [T][H*D].  table may be mapped pinned host memory (see ple_host_alloc).

@@ -22,7 +22,8 @@ import numpy as np
 import torch
 
 from . import capi
-from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_ERR_DEVICE, PLE_ERR_INVALID_ARGUMENT,  # noqa: F401
+from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_DTYPE_FP8_E4M3_GLOBAL, PLE_DTYPE_NVFP4,  # noqa: F401
+                   PLE_ERR_DEVICE, PLE_ERR_INVALID_ARGUMENT,
                    PLE_ERR_UNSUPPORTED, PLE_ERR_WORKSPACE, PLE_MAX_CONTEXT, PLE_MAX_HEADS, PLE_OK)
 
 __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_lookup", "ple_prefetch",
@@ -74,26 +75,45 @@ class HashParams:
 
 
 class Table:
-    """An embedding table: a device tensor, or the device address of mapped pinned host memory."""
+    """An embedding table: a device tensor, or the device address of mapped pinned host memory.
+
+    `row_scales_ptr` is the per-row fp32 scales (PLE_DTYPE_FP8_E4M3) or the
+    one fp32 table scale (PLE_DTYPE_FP8_E4M3_GLOBAL, PLE_DTYPE_NVFP4);
+    `block_scales_ptr` the NVFP4 e4m3fn scale per 16 elements."""
 
     def __init__(self, ptr: int, num_rows: int, dim: int, dtype: int, row_scales_ptr: int | None = None,
-                 keepalive=()):
+                 keepalive=(), block_scales_ptr: int | None = None):
         self.ptr, self.num_rows, self.dim, self.dtype = int(ptr), int(num_rows), int(dim), int(dtype)
         self.row_scales_ptr = row_scales_ptr
+        self.block_scales_ptr = block_scales_ptr
         self._keepalive = keepalive
 
     @classmethod
     def from_tensor(cls, table: torch.Tensor, row_scales: torch.Tensor | None = None) -> "Table":
+        """bf16 [rows][D], or fp8 codes [rows][D] with fp32 scales: [rows] per row, or [1] for the table."""
         if table.dtype in (torch.bfloat16, torch.int16, torch.uint16):
             dt = PLE_DTYPE_BF16
         elif table.dtype in (torch.uint8, torch.float8_e4m3fn):
-            dt = PLE_DTYPE_FP8_E4M3
+            if row_scales is None:
+                raise ValueError("an fp8 table needs its scales")
+            dt = PLE_DTYPE_FP8_E4M3_GLOBAL if row_scales.numel() == 1 and table.shape[0] != 1 else PLE_DTYPE_FP8_E4M3
         else:
             raise ValueError(f"unsupported table dtype {table.dtype}")
         return cls(_ptr(table), table.shape[0], table.shape[1], dt, _ptr(row_scales), (table, row_scales))
 
+    @classmethod
+    def nvfp4(cls, codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale: torch.Tensor) -> "Table":
+        """codes uint8 [rows][D/2] (element 2i in the low nibble of byte i), block_scales
+        uint8 e4m3fn [rows][D/16], tensor_scale fp32 [1]."""
+        rows, half = codes.shape
+        if block_scales.shape != (rows, half // 8) or tensor_scale.numel() != 1:
+            raise ValueError("NVFP4 table: block_scales must be [rows][D/16] and tensor_scale one value")
+        return cls(_ptr(codes), rows, 2 * half, PLE_DTYPE_NVFP4, _ptr(tensor_scale),
+                   (codes, block_scales, tensor_scale), block_scales_ptr=_ptr(block_scales))
+
     def desc(self) -> capi.ple_table_desc:
-        return capi.ple_table_desc(self.ptr, self.num_rows, self.dim, self.dtype, self.row_scales_ptr)
+        return capi.ple_table_desc(self.ptr, self.num_rows, self.dim, self.dtype, self.row_scales_ptr,
+                                   self.block_scales_ptr)
 
 
 class Layer:

@@ -22,6 +22,8 @@ PLE_ERR_DEVICE = 3
 PLE_ERR_WORKSPACE = 4
 PLE_DTYPE_BF16 = 0
 PLE_DTYPE_FP8_E4M3 = 1
+PLE_DTYPE_FP8_E4M3_GLOBAL = 2
+PLE_DTYPE_NVFP4 = 3
 PLE_MAX_HEADS = 32
 PLE_MAX_CONTEXT = 7
 
@@ -37,7 +39,8 @@ class ple_hash_desc(ctypes.Structure):
 
 
 class ple_table_desc(ctypes.Structure):
-    _fields_ = [("table", P), ("num_rows", I64), ("dim", I32), ("dtype", I32), ("row_scales", P)]
+    _fields_ = [("table", P), ("num_rows", I64), ("dim", I32), ("dtype", I32), ("row_scales", P),
+                ("block_scales", P)]
 
 
 class ple_batch_desc(ctypes.Structure):

@@ -97,21 +97,33 @@ int validate_hash(const ple_hash_desc* h, HashParams* hp) {
     return PLE_OK;
 }
 
+// table elements per 16-byte chunk of a stored row
+int table_elems_per_chunk(int dtype) {
+    return dtype == PLE_DTYPE_BF16 ? 8 : (dtype == PLE_DTYPE_NVFP4 ? 32 : 16);
+}
+
 int validate_table(const ple_table_desc* t, int* cpr_log2) {
     if (t == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "table descriptor is NULL");
-    if (t->dtype != PLE_DTYPE_BF16 && t->dtype != PLE_DTYPE_FP8_E4M3)
-        return fail(PLE_ERR_UNSUPPORTED, "table dtype %d is not PLE_DTYPE_BF16 or PLE_DTYPE_FP8_E4M3", t->dtype);
+    if (t->dtype != PLE_DTYPE_BF16 && t->dtype != PLE_DTYPE_FP8_E4M3 && t->dtype != PLE_DTYPE_FP8_E4M3_GLOBAL &&
+        t->dtype != PLE_DTYPE_NVFP4)
+        return fail(PLE_ERR_UNSUPPORTED, "table dtype %d is not one of the PLE_DTYPE_* formats", t->dtype);
     if (t->table == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "table pointer is NULL");
     if (!aligned16(t->table)) return fail(PLE_ERR_INVALID_ARGUMENT, "table pointer is not 16-byte aligned");
     if (t->num_rows < 1 || t->num_rows > ((int64_t)1 << 31))
         return fail(PLE_ERR_INVALID_ARGUMENT, "num_rows %lld outside 1..2^31", (long long)t->num_rows);
     if (t->dim < 1 || t->dim > 8192) return fail(PLE_ERR_INVALID_ARGUMENT, "dim %d outside 1..8192", t->dim);
-    const int elem_per_chunk = t->dtype == PLE_DTYPE_BF16 ? 8 : 16;
+    const int elem_per_chunk = table_elems_per_chunk(t->dtype);
     if (t->dim % elem_per_chunk != 0)
-        return fail(PLE_ERR_UNSUPPORTED, "row of %d elements is not a multiple of 16 bytes", t->dim);
-    if (t->dtype == PLE_DTYPE_FP8_E4M3) {
-        if (t->row_scales == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "fp8 table needs row_scales");
+        return fail(PLE_ERR_UNSUPPORTED, "row of %d elements is not a multiple of 16 bytes (%d elements)", t->dim,
+                    elem_per_chunk);
+    if (t->dtype != PLE_DTYPE_BF16) {
+        if (t->row_scales == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "a quantised table needs row_scales");
         if (!aligned4(t->row_scales)) return fail(PLE_ERR_INVALID_ARGUMENT, "row_scales is not 4-byte aligned");
+    }
+    if (t->dtype == PLE_DTYPE_NVFP4) {
+        if (t->block_scales == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "an NVFP4 table needs block_scales");
+        if (((uintptr_t)t->block_scales & 1) != 0)
+            return fail(PLE_ERR_INVALID_ARGUMENT, "block_scales is not 2-byte aligned");
     }
     const int cpr = t->dim / elem_per_chunk;
     *cpr_log2 = -1;
@@ -229,12 +241,14 @@ LookupArgs lookup_args(const ple_table_desc* t, int H, int cpr_log2, const ple_b
     g.ids_out = ids_out;
     g.table = t->table;
     g.scales = t->row_scales;
+    g.block_scales = t->block_scales;
+    g.scale_stride = t->dtype == PLE_DTYPE_FP8_E4M3 ? 1 : 0;
     g.rows = rows;
     g.num_tokens = T;
     g.num_rows = t->num_rows;
     g.num_heads = H;
     g.dim = t->dim;
-    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dtype == PLE_DTYPE_BF16 ? t->dim / 8 : t->dim / 16);
+    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dim / table_elems_per_chunk(t->dtype));
     g.cpr_log2 = cpr_log2;
     return g;
 }

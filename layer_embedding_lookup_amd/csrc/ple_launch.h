@@ -14,7 +14,8 @@ struct LookupArgs {
     const int32_t* ids_in;
     int32_t* ids_out;
     const void* table;
-    const float* scales;
+    const float* scales;          // fp8: per-row scales (scale_stride 1) or one scale (0); NVFP4: one scale
+    const uint8_t* block_scales;  // NVFP4: e4m3fn code per 16 elements, [num_rows][dim/16]
     uint16_t* rows;
     int64_t num_tokens;
     int64_t num_rows;
@@ -22,9 +23,12 @@ struct LookupArgs {
     int32_t num_heads;
     int32_t dim;
     int32_t tokens_per_wave;
-    int32_t cpr_log2;  // log2(16-byte input chunks per row), or -1
-    int32_t pad;
+    int32_t cpr_log2;      // log2(16-byte input chunks per row), or -1
+    int32_t scale_stride;  // fp8: 1 for one scale per row, 0 for one scale for the table
 };
+
+// kernel-side table formats (the fp8 per-row and global-scale tables share one kernel)
+enum { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 3 };
 
 hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int32_t* qsl, int64_t T, int R,
                             const int32_t* ctx, int32_t* ids, hipStream_t s);

@@ -5,8 +5,8 @@
 // with EOS replacement, the carried ngram_context and int64 wraparound); the
 // row lookup of "PR #54371 [Qwen4Exp] Support UVA PLE-offload and Engram
 // tensor parallelism", 关键源码片段 (embedding lookup, also from pinned host
-// memory); FP8 e4m3fn tables with a scale from "Support PLE-Offload for
-// Qwen3.8-Flash-Next - #53899".
+// memory); FP8 e4m3fn tables with a per-row or a global scale, and NVFP4
+// tables, from "Support PLE-Offload for Qwen3.8-Flash-Next - #53899".
 //
 // Design for CDNA4: each wave owns a few consecutive tokens (at most 64
 // (token, head) rows).  One lane per row computes the ID in registers: the
@@ -76,6 +76,33 @@ __device__ __forceinline__ void dequant16(u32x4 q, float scale, u32x4& lo, u32x4
     }
     lo = u32x4{o[0], o[1], o[2], o[3]};
     hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// NVFP4 x32 (one 16-byte chunk of e2m1 codes, element 2i in the low nibble
+// of byte i) -> 32 bf16 (four 16-byte chunks).  Element value:
+// (e2m1 * e4m3fn(block scale)) * tensor scale; the first product is exact in
+// fp32 (at most 2 x 4 significant bits), the second is one fp32 multiply.
+// The 32 elements span two 16-element blocks; bs holds their two scale codes
+// (low byte first).  v_cvt_scalef32_pk_f32_fp4 with scale 1.0 decodes two
+// codes exactly.
+__device__ __forceinline__ void dequant32_fp4(u32x4 q, uint32_t bs, float tscale, u32x4 (&o)[4]) {
+    const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs, false);  // both block scales, exact
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t r[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float s = k < 2 ? b0.x : b0.y;  // bytes 0..7 -> elements 0..15 -> block 0
+        f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 0);
+        f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 1);
+        f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 2);
+        f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 3);
+        r[4 * k + 0] = pack_bf16x2_canon((v0.x * s) * tscale, (v0.y * s) * tscale);
+        r[4 * k + 1] = pack_bf16x2_canon((v1.x * s) * tscale, (v1.y * s) * tscale);
+        r[4 * k + 2] = pack_bf16x2_canon((v2.x * s) * tscale, (v2.y * s) * tscale);
+        r[4 * k + 3] = pack_bf16x2_canon((v3.x * s) * tscale, (v3.y * s) * tscale);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = u32x4{r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]};
 }
 
 // ID of head h for token t, given its request (r, a) and the raw tokens
@@ -149,26 +176,29 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
         id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
     }
     float scale = 0.f;
-    if (DTYPE == PLE_DTYPE_FP8_E4M3) scale = g.scales[id];
+    if (DTYPE == kFmtFP8) scale = g.scales[(int64_t)id * g.scale_stride];
+    const float tscale = DTYPE == kFmtNVFP4 ? g.scales[0] : 0.f;
 
-    // chunks of 16 input bytes per row: D*2/16 for bf16, D/16 for fp8
-    const int cpr = DTYPE == PLE_DTYPE_BF16 ? (g.dim >> 3) : (g.dim >> 4);
+    // chunks of 16 input bytes per row: D*2/16 for bf16, D/16 for fp8, D/32 for NVFP4
+    const int cpr = DTYPE == kFmtBF16 ? (g.dim >> 3) : (DTYPE == kFmtFP8 ? (g.dim >> 4) : (g.dim >> 5));
     const int shift = g.cpr_log2;  // >= 0 when cpr is a power of two
     const int total = nrows * cpr;
     const char* __restrict__ table = (const char*)g.table;
-    const int64_t row_bytes = DTYPE == PLE_DTYPE_BF16 ? (int64_t)g.dim * 2 : (int64_t)g.dim;
+    const int64_t row_bytes =
+        DTYPE == kFmtBF16 ? (int64_t)g.dim * 2 : (DTYPE == kFmtFP8 ? (int64_t)g.dim : (int64_t)(g.dim >> 1));
     u32x4* __restrict__ out = (u32x4*)(g.rows + t0 * H * (int64_t)g.dim);
 
     for (int base = 0; base < total; base += kWave * UNROLL) {
         u32x4 v[UNROLL];
         float sc[UNROLL];
+        uint32_t bsc[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + u * kWave + lane;
             int row = shift >= 0 ? (idx >> shift) : (idx / cpr);
             row = row < nrows ? row : nrows - 1;
             const int rid = __shfl(id, row, kWave);
-            if (DTYPE == PLE_DTYPE_FP8_E4M3) sc[u] = __shfl(scale, row, kWave);
+            if (DTYPE == kFmtFP8) sc[u] = __shfl(scale, row, kWave);
             if (idx < total) {
                 const int ch = idx - row * cpr;
                 const u32x4* src = (const u32x4*)(table + (int64_t)rid * row_bytes) + ch;
@@ -177,19 +207,27 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
 #else
                 v[u] = *src;
 #endif
+                // the two block-scale codes of this chunk's 32 elements
+                if (DTYPE == kFmtNVFP4)
+                    bsc[u] = *(const uint16_t*)(g.block_scales + (int64_t)rid * (g.dim >> 4) + 2 * ch);
             }
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + u * kWave + lane;
             if (idx < total) {
-                if (DTYPE == PLE_DTYPE_BF16) {
+                if (DTYPE == kFmtBF16) {
                     store16(out + idx, v[u]);
-                } else {
+                } else if (DTYPE == kFmtFP8) {
                     u32x4 lo, hi;
                     dequant16(v[u], sc[u], lo, hi);
                     store16(out + 2 * idx, lo);
                     store16(out + 2 * idx + 1, hi);
+                } else {
+                    u32x4 o[4];
+                    dequant32_fp4(v[u], bsc[u], tscale, o);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) store16(out + 4 * idx + k, o[k]);
                 }
             }
         }
@@ -269,10 +307,14 @@ static hipError_t launch_lookup_t(const HashParams& hp, const LookupArgs& g, hip
 
 hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s) {
     if (dtype == PLE_DTYPE_BF16)
-        return mode == kModeHash ? launch_lookup_t<PLE_DTYPE_BF16, kModeHash>(hp, g, s)
-                                 : launch_lookup_t<PLE_DTYPE_BF16, kModeIds>(hp, g, s);
-    return mode == kModeHash ? launch_lookup_t<PLE_DTYPE_FP8_E4M3, kModeHash>(hp, g, s)
-                             : launch_lookup_t<PLE_DTYPE_FP8_E4M3, kModeIds>(hp, g, s);
+        return mode == kModeHash ? launch_lookup_t<kFmtBF16, kModeHash>(hp, g, s)
+                                 : launch_lookup_t<kFmtBF16, kModeIds>(hp, g, s);
+    if (dtype == PLE_DTYPE_NVFP4)
+        return mode == kModeHash ? launch_lookup_t<kFmtNVFP4, kModeHash>(hp, g, s)
+                                 : launch_lookup_t<kFmtNVFP4, kModeIds>(hp, g, s);
+    // per-row and global-scale fp8 (the scale stride tells them apart)
+    return mode == kModeHash ? launch_lookup_t<kFmtFP8, kModeHash>(hp, g, s)
+                             : launch_lookup_t<kFmtFP8, kModeIds>(hp, g, s);
 }
 
 }  // namespace ple

@@ -45,6 +45,10 @@ def _lib():
     lib.orc_ngram_ids.restype = ctypes.c_int
     lib.orc_gather_bf16.argtypes = [P, I32, P, I64, P]
     lib.orc_gather_fp8.argtypes = [P, P, I32, P, I64, P]
+    lib.orc_gather_fp8_global.argtypes = [P, ctypes.c_float, I32, P, I64, P]
+    lib.orc_gather_nvfp4.argtypes = [P, P, ctypes.c_float, I32, P, I64, P]
+    lib.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1_value.restype = D
     lib.orc_e4m3fn_value.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3fn_value.restype = D
     lib.orc_bf16_from_double.argtypes = [D]
@@ -105,6 +109,32 @@ def gather_fp8(codes, scales, ids):
     rows = np.empty((ids.shape[0], D), dtype=np.uint16)
     _lib().orc_gather_fp8(_p(codes), _p(scales), D, _p(ids), ids.shape[0], _p(rows))
     return rows
+
+
+def gather_fp8_global(codes, scale, ids):
+    """rows [n, D] (bf16 bits) from fp8 codes with one fp32 scale for the table."""
+    ids = _c(ids, np.int32).reshape(-1)
+    codes = _c(codes, np.uint8)
+    D = codes.shape[1]
+    rows = np.empty((ids.shape[0], D), dtype=np.uint16)
+    _lib().orc_gather_fp8_global(_p(codes), float(np.float32(scale)), D, _p(ids), ids.shape[0], _p(rows))
+    return rows
+
+
+def gather_nvfp4(codes, block_scales, tensor_scale, ids):
+    """rows [n, D] (bf16 bits) from NVFP4 codes [rows, D/2], e4m3fn block scales [rows, D/16]."""
+    ids = _c(ids, np.int32).reshape(-1)
+    codes = _c(codes, np.uint8)
+    bs = _c(block_scales, np.uint8)
+    D = codes.shape[1] * 2
+    assert bs.shape == (codes.shape[0], D // 16)
+    rows = np.empty((ids.shape[0], D), dtype=np.uint16)
+    _lib().orc_gather_nvfp4(_p(codes), _p(bs), float(np.float32(tensor_scale)), D, _p(ids), ids.shape[0], _p(rows))
+    return rows
+
+
+def e2m1_value(code: int) -> float:
+    return _lib().orc_e2m1_value(code)
 
 
 def e4m3fn_value(code: int) -> float:
@@ -174,14 +204,21 @@ def prefill(batch_ids_args: dict, table, scales, hidden, kv_weight, conv_weight,
     T, H = ids.shape
 
     def gather(sel):
-        return gather_bf16(table, sel) if scales is None else gather_fp8(table, scales, sel)
+        if scales is None:
+            return gather_bf16(table, sel)
+        if isinstance(scales, tuple):  # NVFP4: (block_scales, tensor_scale)
+            return gather_nvfp4(table, scales[0], scales[1], sel)
+        if np.size(scales) == 1 and table.shape[0] != 1:
+            return gather_fp8_global(table, np.asarray(scales).reshape(-1)[0], sel)
+        return gather_fp8(table, scales, sel)
 
     if tokens is None:
         rows = gather(ids).reshape(T, -1)
         kv = kv_proj(rows, kv_weight)
     else:
         need = conv_taps(tokens, qsl, conv_weight.shape[1], dilation)
-        rows = np.zeros((T, H * table.shape[1]), dtype=np.uint16)
+        D = table.shape[1] * (2 if isinstance(scales, tuple) else 1)
+        rows = np.zeros((T, H * D), dtype=np.uint16)
         rows[need] = gather(ids[need]).reshape(len(need), -1)
         kv = np.zeros((T, kv_weight.shape[0]), dtype=np.uint16)
         kv[need] = kv_proj(rows[need], kv_weight)

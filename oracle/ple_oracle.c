@@ -169,6 +169,42 @@ void orc_gather_fp8(const uint8_t* codes, const float* scales, int32_t dim, cons
     }
 }
 
+void orc_gather_fp8_global(const uint8_t* codes, float scale, int32_t dim, const int32_t* ids, int64_t n,
+                           uint16_t* rows) {
+    for (int64_t k = 0; k < n; ++k) {
+        int64_t id = ids[k];
+        for (int32_t c = 0; c < dim; ++c) {
+            float value = (float)orc_e4m3fn_value(codes[id * dim + c]); /* exact in fp32 */
+            float product = value * scale;                              /* one fp32 multiply */
+            rows[k * dim + c] = orc_bf16_from_double((double)product);
+        }
+    }
+}
+
+double orc_e2m1_value(uint8_t code) {
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -mag : mag;
+}
+
+void orc_gather_nvfp4(const uint8_t* codes, const uint8_t* block_scales, float tensor_scale, int32_t dim,
+                      const int32_t* ids, int64_t n, uint16_t* rows) {
+    const int64_t row_bytes = dim / 2, row_blocks = dim / 16;
+    for (int64_t k = 0; k < n; ++k) {
+        int64_t id = ids[k];
+        for (int32_t c = 0; c < dim; ++c) {
+            uint8_t byte = codes[id * row_bytes + c / 2];
+            uint8_t code = (c % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);
+            double block = orc_e4m3fn_value(block_scales[id * row_blocks + c / 16]);
+            float scaled = (float)(orc_e2m1_value(code) * block); /* exact: 2 x 4 significant bits */
+            float value = scaled * tensor_scale;                  /* one fp32 multiply */
+            rows[k * dim + c] = orc_bf16_from_double((double)value);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* merged key/value projection                                               */
 /* ------------------------------------------------------------------------ */

@@ -16,7 +16,9 @@
  *        merged kv_proj) and 关键源码片段 (compute_ngram_ids, the ids kernel's
  *        arguments and its per-shift loop).
  *   [P4] "Support PLE-Offload for Qwen3.8-Flash-Next - #53899" - the report
- *        on FP8 PLE tables (float8_e4m3fn with a weight scale).
+ *        on FP8 PLE tables (float8_e4m3fn with a weight scale; the review
+ *        thread on one global weight scale) and the walkthrough naming NVFP4
+ *        embedding support.
  * Where the pages leave a step open the readings are listed per function.
  *
  * Parity pins: every function here is checked by the CPU test suite against
@@ -57,8 +59,27 @@ void orc_gather_bf16(const uint16_t* table, int32_t dim, const int32_t* ids, int
 void orc_gather_fp8(const uint8_t* codes, const float* scales, int32_t dim, const int32_t* ids, int64_t n,
                     uint16_t* rows);
 
+/* The same with one scale for the whole table ([P4] review thread: an FP8
+ * PLE table with one global weight scale). */
+void orc_gather_fp8_global(const uint8_t* codes, float scale, int32_t dim, const int32_t* ids, int64_t n,
+                           uint16_t* rows);
+
 /* OCP float8 e4m3fn value of a code (NaN for 0x7F and 0xFF). */
 double orc_e4m3fn_value(uint8_t code);
+
+/* OCP MX FP4 e2m1 value of a 4-bit code: sign bit 3, exponent bits 2..1
+ * (bias 1), mantissa bit 0; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double orc_e2m1_value(uint8_t code);
+
+/* NVFP4 rows ([P4] walkthrough names NVFP4 embedding support; the layout is
+ * the plain reading of the public format, the pages print none): a row of dim
+ * elements is dim/2 bytes, element c in byte c/2 (low nibble for even c); its
+ * 16-element block b has the e4m3fn scale block_scales[row][b]; one fp32
+ * tensor_scale for the table.
+ * rows[k][c] = bf16(float(e2m1(code) * e4m3fn(block scale)) * tensor_scale):
+ * the first product is exact, then one fp32 multiply, then nearest-even. */
+void orc_gather_nvfp4(const uint8_t* codes, const uint8_t* block_scales, float tensor_scale, int32_t dim,
+                      const int32_t* ids, int64_t n, uint16_t* rows);
 
 /* bfloat16 nearest-even rounding of a real value; NaN -> 0x7FC0. */
 uint16_t orc_bf16_from_double(double x);

@@ -493,3 +493,76 @@ def test_cu_masked_stream_prefetch():
     finally:
         torch.cuda.synchronize()
         ple.ple_stream_destroy(s)
+
+
+# ------------------------------------------------------------------ global-scale fp8 and NVFP4 tables
+
+def _nvfp4_dev(codes, bs, t):
+    keep = (dev(codes), dev(bs), dev(np.asarray([t], dtype=np.float32)))
+    return ple.Table.nvfp4(*keep), keep
+
+
+def test_lookup_fp8_global_scale():
+    cfg = _small_fp8_cfg()
+    b = wl.make_batch(cfg)
+    q, _ = wl.make_table(cfg)
+    s = np.float32(0.0173)
+    tb = ple.Table.from_tensor(dev(q), dev(np.asarray([s], np.float32)))
+    assert tb.dtype == ple.PLE_DTYPE_FP8_E4M3_GLOBAL
+    ids = oracle_ids(b)
+    rows = ple.ple_lookup(hash_params(b), tb, dev(b.input_ids), dev(b.qsl))
+    np.testing.assert_array_equal(host_bits(rows), oracle.gather_fp8_global(q, s, ids).reshape(cfg.T, -1))
+
+
+def test_fp8_global_every_code():
+    rng = np.random.default_rng(11)
+    codes = np.stack([rng.permutation(256) for _ in range(32)]).astype(np.uint8)
+    ids = rng.integers(0, 32, size=(40, 2)).astype(np.int32)
+    for s in (np.float32(1.0), np.float32(2.0 ** -30), np.float32(7.5e28)):
+        tb = ple.Table.from_tensor(dev(codes), dev(np.asarray([s], np.float32)))
+        rows = ple.ple_gather(tb, dev(ids))
+        np.testing.assert_array_equal(host_bits(rows), oracle.gather_fp8_global(codes, s, ids).reshape(40, -1))
+
+
+def test_nvfp4_golden_cases_on_gpu():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        D = case["dim"]
+        codes = np.asarray(case["codes"], dtype=np.uint8).reshape(1, D // 2)
+        bs = np.asarray(case["block_scales"], dtype=np.uint8).reshape(1, D // 16)
+        t = np.uint32(int(case["tensor_scale_bits"], 16)).view(np.float32)
+        tb, keep = _nvfp4_dev(codes, bs, t)
+        rows = ple.ple_gather(tb, dev(np.zeros((1, 1), np.int32)))
+        assert host_bits(rows)[0].tolist() == [int(x, 16) for x in case["expected_bf16"]], case["name"]
+
+
+@pytest.mark.parametrize("D", [32, 64, 512, 96])
+def test_gather_nvfp4_every_code(D):
+    rng = np.random.default_rng(D + 1)
+    nrows = 500
+    codes = rng.integers(0, 256, size=(nrows, D // 2), dtype=np.uint8)
+    bs = rng.integers(0, 256, size=(nrows, D // 16), dtype=np.uint8)  # includes NaN and zero scales
+    t = np.float32(0.031)
+    ids = rng.integers(0, nrows, size=(211, 3)).astype(np.int32)
+    tb, keep = _nvfp4_dev(codes, bs, t)
+    rows = ple.ple_gather(tb, dev(ids))
+    np.testing.assert_array_equal(host_bits(rows), oracle.gather_nvfp4(codes, bs, t, ids).reshape(211, -1))
+
+
+def test_lookup_nvfp4_and_fused_prefill():
+    cfg = wl.CONFIGS[1]
+    b = wl.make_batch(cfg, with_context=True, with_state=True)
+    codes, bs, t = wl.make_nvfp4_table(cfg.num_rows, cfg.D, cfg.seed)
+    tb, keep = _nvfp4_dev(codes, bs, t)
+    ids = oracle_ids(b)
+    rows = ple.ple_lookup(hash_params(b), tb, dev(b.input_ids), dev(b.qsl), ngram_context=dev(b.ngram_context))
+    np.testing.assert_array_equal(host_bits(rows), oracle.gather_nvfp4(codes, bs, t, ids).reshape(cfg.T, -1))
+    kvw, cw, hidden = wl.make_kv_weight(cfg), wl.make_conv_weight(cfg), wl.make_hidden(cfg)
+    L = ple.Layer(hash_params(b), tb, dev_bf16(kvw), dev_bf16(cw), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    out = ple.ple_prefill_fused(L, dev(b.input_ids), dev(b.qsl), dev_bf16(hidden),
+                                ngram_context=dev(b.ngram_context), conv_state=dev_bf16(b.conv_state))
+    ref = _oracle_chain(cfg, b, codes, (bs, t), kvw, cw, hidden)
+    assert np.abs(bf16_f64(host_bits(out)) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL

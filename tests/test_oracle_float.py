@@ -10,6 +10,8 @@
 * conv: torch conv1d with dilation per request, Kc = 1, impulse response,
   chunked == whole with carried state ("PR #54517 ...", 实现拆解 item 2).
 """
+import json
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -313,3 +315,80 @@ def test_gather_fp8_multiply_rounds_in_fp32_first():
     got = oracle.gather_fp8(np.asarray([[0x39]], np.uint8), np.asarray([found], np.float32),
                             np.asarray([0], np.int32))
     assert got[0, 0] == 0x3F82
+
+
+# ---------------------------------------------------------------- global-scale fp8 and NVFP4
+
+def test_gather_fp8_global_vs_torch():
+    """One scale for the table: torch's float8_e4m3fn decode, one fp32 multiply, bf16."""
+    rng = np.random.default_rng(7)
+    rows, D = 200, 64
+    codes = rng.integers(0, 256, size=(rows, D), dtype=np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    ids = rng.integers(0, rows, size=77).astype(np.int32)
+    for scale in (np.float32(0.0123), np.float32(3.5), np.float32(2.0 ** -20)):
+        got = oracle.gather_fp8_global(codes, scale, ids)
+        f = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+        ref = (f * torch.tensor(scale)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[ids]
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_gather_fp8_global_equals_per_row_with_equal_scales():
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 256, size=(50, 32), dtype=np.uint8)
+    ids = rng.integers(0, 50, size=40).astype(np.int32)
+    s = np.float32(0.37)
+    np.testing.assert_array_equal(oracle.gather_fp8_global(codes, s, ids),
+                                  oracle.gather_fp8(codes, np.full(50, s, np.float32), ids))
+
+
+def _nvfp4_golden():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_cases.json")) as f:
+        return json.load(f)
+
+
+def test_e2m1_values_match_the_format():
+    want = _nvfp4_golden()["e2m1_values"]
+    got = [oracle.e2m1_value(c) for c in range(16)]
+    assert got == want
+    assert [np.signbit(v) for v in got] == [c >= 8 for c in range(16)]
+
+
+@pytest.mark.parametrize("case", _nvfp4_golden()["cases"], ids=lambda c: c["name"])
+def test_gather_nvfp4_golden(case):
+    D = case["dim"]
+    codes = np.asarray(case["codes"], dtype=np.uint8).reshape(1, D // 2)
+    bs = np.asarray(case["block_scales"], dtype=np.uint8).reshape(1, D // 16)
+    t = np.uint32(int(case["tensor_scale_bits"], 16)).view(np.float32)
+    got = oracle.gather_nvfp4(codes, bs, t, np.asarray([0], np.int32))[0]
+    want = [int(x, 16) for x in case["expected_bf16"]]
+    assert got.tolist() == want
+
+
+def test_gather_nvfp4_unit_code_reduces_to_global_fp8():
+    """e2m1 code 2 is exactly 1.0, so each element is e4m3fn(block scale) times the
+    table scale: the global-scale fp8 gather (pinned against torch) on the block codes."""
+    rng = np.random.default_rng(9)
+    rows, D = 64, 64
+    bs = rng.integers(0, 256, size=(rows, D // 16), dtype=np.uint8)
+    codes = np.full((rows, D // 2), 0x22, dtype=np.uint8)
+    ids = rng.integers(0, rows, size=30).astype(np.int32)
+    t = np.float32(0.0731)
+    got = oracle.gather_nvfp4(codes, bs, t, ids)
+    want = oracle.gather_fp8_global(np.repeat(bs, 16, axis=1), t, ids)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_gather_nvfp4_unit_scales_give_the_code_values():
+    rng = np.random.default_rng(10)
+    codes = rng.integers(0, 256, size=(10, 16), dtype=np.uint8)
+    bs = np.full((10, 2), 0x38, dtype=np.uint8)  # e4m3fn 1.0
+    got = oracle.gather_nvfp4(codes, bs, np.float32(1.0), np.arange(10, dtype=np.int32))
+    e2m1 = _nvfp4_golden()["e2m1_values"]
+    for r in range(10):
+        for c in range(32):
+            byte = int(codes[r, c // 2])
+            v = e2m1[byte & 15] if c % 2 == 0 else e2m1[byte >> 4]
+            assert oracle.bf16_value(int(got[r, c])) == v
+            assert np.signbit(oracle.bf16_value(int(got[r, c]))) == np.signbit(v)

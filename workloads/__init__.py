@@ -54,6 +54,7 @@ def _lib():
     lib.gen_uniform_bf16.argtypes = [P, I64, U64, D, D, I]
     lib.gen_fp8_table.argtypes = [P, P, I64, ctypes.c_int32, U64, D, I]
     lib.gen_fp8_table.restype = ctypes.c_int
+    lib.gen_uniform_bytes.argtypes = [P, I64, U64, ctypes.c_int, ctypes.c_int, I]
     lib.gen_store_bf16.argtypes = [ctypes.c_float]
     lib.gen_store_bf16.restype = ctypes.c_uint16
     lib.gen_store_e4m3fn.argtypes = [ctypes.c_float]
@@ -365,6 +366,29 @@ def make_table(cfg: Config, seed: int | None = None):
     sc = np.empty((cfg.num_rows,), dtype=np.float32)
     fill_table(cfg, q, sc, seed=seed)
     return q, sc
+
+
+def uniform_bytes(shape, seed: int, lo: int, hi: int, threads=None) -> np.ndarray:
+    """uint8 array, each entry uniform over the integers lo..hi (SplitMix64 at the entry's index)."""
+    out = np.empty(shape, dtype=np.uint8)
+    _lib().gen_uniform_bytes(out.ctypes.data, out.size, seed & MASK64, lo, hi, threads or default_threads())
+    return out
+
+
+# NVFP4 table recipe (no page fixes one): every byte of codes uniform over
+# 0..255 (so both nibbles cover all 16 e2m1 codes), block-scale codes uniform
+# over the e4m3fn codes 0x28..0x48 (0.25 .. 4), and a table scale of 0.005,
+# which puts typical |values| near the bf16 table's 0.02.
+NVFP4_BLOCK_SCALE_CODES = (0x28, 0x48)
+NVFP4_TENSOR_SCALE = np.float32(0.005)
+S_NVFP4_CODES, S_NVFP4_SCALES = 101, 102
+
+
+def make_nvfp4_table(num_rows: int, dim: int, seed: int):
+    """(codes uint8 [rows, D/2], block scales uint8 [rows, D/16], tensor scale float32)."""
+    codes = uniform_bytes((num_rows, dim // 2), stream_seed(seed, S_NVFP4_CODES), 0, 255)
+    bs = uniform_bytes((num_rows, dim // 16), stream_seed(seed, S_NVFP4_SCALES), *NVFP4_BLOCK_SCALE_CODES)
+    return codes, bs, NVFP4_TENSOR_SCALE
 
 
 def make_hidden(cfg: Config, seed: int | None = None, T: int | None = None) -> np.ndarray:

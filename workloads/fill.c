@@ -88,7 +88,7 @@ typedef struct {
     int32_t dim;
 } job_t;
 
-enum { JOB_NORMAL_BF16 = 0, JOB_UNIFORM_BF16 = 1, JOB_FP8_ROWS = 2, JOB_NORMAL_F32 = 3 };
+enum { JOB_NORMAL_BF16 = 0, JOB_UNIFORM_BF16 = 1, JOB_FP8_ROWS = 2, JOB_NORMAL_F32 = 3, JOB_UNIFORM_BYTES = 4 };
 
 static void run_job(job_t* j) {
     if (j->kind == JOB_NORMAL_BF16) {
@@ -99,6 +99,13 @@ static void run_job(job_t* j) {
         uint16_t* o = (uint16_t*)j->out;
         for (int64_t i = j->begin; i < j->end; ++i)
             o[i] = store_bf16((float)(j->a + (j->b - j->a) * uniform01(j->seed, (uint64_t)i)));
+    } else if (j->kind == JOB_UNIFORM_BYTES) { /* integers in [a, b] */
+        uint8_t* o = (uint8_t*)j->out;
+        const double span = j->b - j->a + 1.0;
+        for (int64_t i = j->begin; i < j->end; ++i) {
+            double v = j->a + floor(span * uniform01(j->seed, (uint64_t)i));
+            o[i] = (uint8_t)(v > j->b ? j->b : v);
+        }
     } else if (j->kind == JOB_NORMAL_F32) {
         float* o = (float*)j->out;
         for (int64_t i = j->begin; i < j->end; ++i)
@@ -184,6 +191,12 @@ int gen_fp8_table(uint8_t* q, float* scale, int64_t rows, int32_t dim, uint64_t 
     job_t j = {JOB_FP8_ROWS, q, scale, 0, 0, seed, sigma, 0.0, dim};
     run_parallel(j, rows, nthreads);
     return 0;
+}
+
+/* out[i] = lo + floor((hi - lo + 1) * uniform(seed, i)), 0 <= lo <= hi <= 255 */
+void gen_uniform_bytes(uint8_t* out, int64_t n, uint64_t seed, int lo, int hi, int nthreads) {
+    job_t j = {JOB_UNIFORM_BYTES, out, NULL, 0, 0, seed, (double)lo, (double)hi, 0};
+    run_parallel(j, n, nthreads);
 }
 
 /* Encoding helpers exposed so tests can check the generator's own encoders. */
