@@ -45,9 +45,10 @@ def main() -> int:
     ap.add_argument("--prefetch-cus", type=int, default=32, help="CUs of the host-table prefetch stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="prefill-8k-bf16-hbm",
-                    choices=["prefill-8k-bf16-hbm", "prefill-16k-fp8-hbm", "prefill-8k-bf16-host"],
-                    help="the default is the benchmark line; the others report the fp8-table and "
-                         "host-resident-table variants")
+                    choices=["prefill-8k-bf16-hbm", "prefill-16k-fp8-hbm", "prefill-16k-fp8global-hbm",
+                             "prefill-8k-nvfp4-hbm", "prefill-8k-bf16-host"],
+                    help="the default is the benchmark line; the others report the fp8-table (per-row or "
+                         "one global scale), NVFP4-table and host-resident-table variants")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -64,13 +65,24 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.workload == "prefill-8k-bf16-host":
         return bench_host_table(args)
-    cfg = wl.CONFIGS[3] if args.workload == "prefill-8k-bf16-hbm" else wl.CONFIGS[4]
+    # table format of the workload; the batch, projection and conv are those of
+    # the 8k prefill (bf16, NVFP4) or the 16k prefill (fp8 tables)
+    fmt = {"prefill-8k-bf16-hbm": "bf16", "prefill-16k-fp8-hbm": "fp8", "prefill-16k-fp8global-hbm": "fp8-global",
+           "prefill-8k-nvfp4-hbm": "nvfp4"}[args.workload]
+    cfg = wl.CONFIGS[3] if fmt in ("bf16", "nvfp4") else wl.CONFIGS[4]
     L = args.layers
-    log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} rows={cfg.num_rows} D={cfg.D} N={cfg.N}")
+    log(f"workload {args.workload}: T={cfg.T} H={cfg.H} rows={cfg.num_rows} D={cfg.D} N={cfg.N}")
     b = wl.make_batch(cfg, layers=L)
     log("generating the table on the host")
     t0 = time.time()
-    table_h, scales_h = wl.make_table(cfg)
+    if fmt == "nvfp4":
+        codes_h, bs_h, tscale = wl.make_nvfp4_table(cfg.num_rows, cfg.D, cfg.seed)
+        table_h, scales_h = codes_h, (bs_h, tscale)
+    else:
+        table_h, scales_h = wl.make_table(cfg)
+        if fmt == "fp8-global":
+            # the same codes with one scale for the table: the largest per-row scale
+            scales_h = np.asarray([scales_h.max()], dtype=np.float32)
     log(f"table ready in {time.time() - t0:.1f}s; copying to HBM")
 
     def bf(a):
@@ -79,9 +91,12 @@ def main() -> int:
     def it(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    if cfg.table_dtype == "bf16":
+    if fmt == "bf16":
         table = bf(table_h)
         tb = ple.Table.from_tensor(table)
+    elif fmt == "nvfp4":
+        table = it(table_h)
+        tb = ple.Table.nvfp4(table, it(scales_h[0]), it(np.asarray([scales_h[1]], dtype=np.float32)))
     else:
         table, scales = it(table_h), it(scales_h)
         tb = ple.Table.from_tensor(table, scales)
@@ -150,7 +165,7 @@ def main() -> int:
     # embedding gather on the same IDs (an index_select into the same output).
     write_only_ms = timed(lambda i: rows.fill_(1.0), 4 * L)
     torch_gather_ms = None
-    if cfg.table_dtype == "bf16":
+    if fmt == "bf16":
         ids_l = [ple.ple_ngram_ids(hashes[l], toks, qsl).view(-1).long() for l in range(L)]
         rows_flat = rows.view(T * H, D)
         torch_gather_ms = timed(lambda i: torch.index_select(table, 0, ids_l[i % L], out=rows_flat), 4 * L)
@@ -164,7 +179,9 @@ def main() -> int:
     del copy_src, copy_dst
 
     R = b.R
-    row_read = D * 2 if cfg.table_dtype == "bf16" else D + 4  # fp8 codes + the row's scale
+    # bytes read per (token, head) row: bf16 row; fp8 codes (+ the row's scale);
+    # NVFP4 codes + block scales
+    row_read = {"bf16": D * 2, "fp8": D + 4, "fp8-global": D, "nvfp4": D // 2 + D // 16}[fmt]
     lookup_bytes = T * H * (row_read + D * 2) + T * 4 + (R + 1) * 4
     lookup_gbps = lookup_bytes / (lookup_ms * 1e-3) / 1e9
     kv_flops = 2.0 * T * (H * D) * (2 * N)
@@ -175,7 +192,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, b, table_h, scales_h, kv_ws_h[0], conv_w_h, hidden_h, args.cpu_sample_tokens)
+        cpu = cpu_baseline(cfg, b, table_h, scales_h, kv_ws_h[0], conv_w_h, hidden_h, args.cpu_sample_tokens,
+                           args.workload)
 
     line = {
         "metric": METRIC,
@@ -190,15 +208,15 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "requests": R, "heads": H, "orders": [2, 3],
-                   "table_rows": cfg.num_rows, "dim": D, "table_dtype": cfg.table_dtype, "table_location": "hbm",
+        "config": {"workload": args.workload, "tokens": T, "requests": R, "heads": H, "orders": [2, 3],
+                   "table_rows": cfg.num_rows, "dim": D, "table_dtype": fmt, "table_location": "hbm",
                    "hidden": N, "kv_proj": [H * D, 2 * N], "conv": [cfg.conv_kernel, cfg.conv_dilation],
                    "layers_rotated": L},
         "roofline": {"kernel": "kv_proj (MFMA bf16 GEMM)", "bound": "mfma",
                      "achieved": round(kv_tflops, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kv_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(cfg.name), "traffic_unit": "bytes per launch"},
-        "lookup": {"kernel": "fused ids+gather" + ("" if cfg.table_dtype == "bf16" else "+fp8 dequant"),
+        "lookup": {"kernel": "fused ids+gather" + ("" if fmt == "bf16" else f"+{fmt} dequant"),
                    "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
                    "frac_copy_ceiling": round(lookup_gbps / copy_gbps, 4),
@@ -363,7 +381,7 @@ def bench_host_table(args):
     return 0
 
 
-def cpu_baseline(cfg, b, table_h, scales_h, kvw_h, conv_w_h, hidden_h, n_tokens):
+def cpu_baseline(cfg, b, table_h, scales_h, kvw_h, conv_w_h, hidden_h, n_tokens, workload):
     """The oracle, single-threaded, on a bounded sample: the first n_tokens of
     the batch (whole requests, the last one cut to a prefix chunk; by causality
     their outputs equal the full batch's) through the whole path."""
@@ -386,7 +404,7 @@ def cpu_baseline(cfg, b, table_h, scales_h, kvw_h, conv_w_h, hidden_h, n_tokens)
                    eps=cfg.eps)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} tokens ({R} requests) of the {cfg.name} batch, whole path "
+            "sample": f"first {n} tokens ({R} requests) of the {workload} batch, whole path "
                       f"(ids, gather, kv_proj, gate, conv), single-threaded C, {dt:.1f} s"}
 
 

@@ -125,7 +125,7 @@ int validate_table(const ple_table_desc* t, int* cpr_log2) {
         if (((uintptr_t)t->block_scales & 1) != 0)
             return fail(PLE_ERR_INVALID_ARGUMENT, "block_scales is not 2-byte aligned");
     }
-    const int cpr = t->dim / elem_per_chunk;
+    const int cpr = t->dim / 8;  // 16-byte output chunks per row
     *cpr_log2 = -1;
     if ((cpr & (cpr - 1)) == 0)
         for (int s = 0; s < 31; ++s)
@@ -248,7 +248,7 @@ LookupArgs lookup_args(const ple_table_desc* t, int H, int cpr_log2, const ple_b
     g.num_rows = t->num_rows;
     g.num_heads = H;
     g.dim = t->dim;
-    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dim / table_elems_per_chunk(t->dtype));
+    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dim / 8, t->dtype);
     g.cpr_log2 = cpr_log2;
     return g;
 }

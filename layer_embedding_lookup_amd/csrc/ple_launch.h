@@ -23,7 +23,7 @@ struct LookupArgs {
     int32_t num_heads;
     int32_t dim;
     int32_t tokens_per_wave;
-    int32_t cpr_log2;      // log2(16-byte input chunks per row), or -1
+    int32_t cpr_log2;      // log2(16-byte output chunks per row), or -1
     int32_t scale_stride;  // fp8: 1 for one scale per row, 0 for one scale for the table
 };
 
@@ -34,7 +34,7 @@ hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int3
                             const int32_t* ctx, int32_t* ids, hipStream_t s);
 hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T, int R, int C, int32_t eos,
                               const int32_t* ctx, int32_t* ctx_out, hipStream_t s);
-int lookup_tokens_per_wave(int H, int chunks_per_row);
+int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype);
 hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s);
 
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,

@@ -22,8 +22,15 @@
 
 // Tuning knobs (compile-time): 16-byte loads in flight per lane, and whether
 // table reads / row writes carry the non-temporal hint.
+// Output chunks (16 bytes) per lane per pass, by table format.
 #ifndef PLE_LOOKUP_LOADS
 #define PLE_LOOKUP_LOADS 16
+#endif
+#ifndef PLE_LOOKUP_LOADS_FP8
+#define PLE_LOOKUP_LOADS_FP8 16
+#endif
+#ifndef PLE_LOOKUP_LOADS_FP4
+#define PLE_LOOKUP_LOADS_FP4 16
 #endif
 #ifndef PLE_LOOKUP_NT_LOAD
 #define PLE_LOOKUP_NT_LOAD 1
@@ -62,47 +69,34 @@ __global__ __launch_bounds__(256) void context_out_kernel(const int32_t* __restr
     }
 }
 
-// fp8 e4m3fn x16 (one 16-byte chunk) -> 16 bf16 (two 16-byte chunks), each
-// value float(code) * scale in fp32, then round to nearest even.
-__device__ __forceinline__ void dequant16(u32x4 q, float scale, u32x4& lo, u32x4& hi) {
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-        f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-        o[2 * k] = pack_bf16x2_canon(a.x * scale, a.y * scale);
-        o[2 * k + 1] = pack_bf16x2_canon(b.x * scale, b.y * scale);
-    }
-    lo = u32x4{o[0], o[1], o[2], o[3]};
-    hi = u32x4{o[4], o[5], o[6], o[7]};
+// fp8 e4m3fn x8 (8 bytes) -> 8 bf16 (one 16-byte chunk), each value
+// float(code) * scale in fp32, then round to nearest even.
+__device__ __forceinline__ u32x4 dequant8_fp8(uint32_t q0, uint32_t q1, float scale) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q0, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q0, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q1, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q1, true);
+    return u32x4{pack_bf16x2_canon(a.x * scale, a.y * scale), pack_bf16x2_canon(b.x * scale, b.y * scale),
+                 pack_bf16x2_canon(c.x * scale, c.y * scale), pack_bf16x2_canon(d.x * scale, d.y * scale)};
 }
 
-// NVFP4 x32 (one 16-byte chunk of e2m1 codes, element 2i in the low nibble
-// of byte i) -> 32 bf16 (four 16-byte chunks).  Element value:
-// (e2m1 * e4m3fn(block scale)) * tensor scale; the first product is exact in
+// NVFP4 x8 (4 bytes of e2m1 codes, element 2i in the low nibble of byte i;
+// all 8 in one 16-element block) -> 8 bf16.  Element value:
+// (e2m1 * e4m3fn(block scale)) * table scale; the first product is exact in
 // fp32 (at most 2 x 4 significant bits), the second is one fp32 multiply.
-// The 32 elements span two 16-element blocks; bs holds their two scale codes
-// (low byte first).  v_cvt_scalef32_pk_f32_fp4 with scale 1.0 decodes two
-// codes exactly.
-__device__ __forceinline__ void dequant32_fp4(u32x4 q, uint32_t bs, float tscale, u32x4 (&o)[4]) {
-    const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs, false);  // both block scales, exact
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t r[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float s = k < 2 ? b0.x : b0.y;  // bytes 0..7 -> elements 0..15 -> block 0
-        f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 0);
-        f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 1);
-        f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 2);
-        f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 3);
-        r[4 * k + 0] = pack_bf16x2_canon((v0.x * s) * tscale, (v0.y * s) * tscale);
-        r[4 * k + 1] = pack_bf16x2_canon((v1.x * s) * tscale, (v1.y * s) * tscale);
-        r[4 * k + 2] = pack_bf16x2_canon((v2.x * s) * tscale, (v2.y * s) * tscale);
-        r[4 * k + 3] = pack_bf16x2_canon((v3.x * s) * tscale, (v3.y * s) * tscale);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = u32x4{r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]};
+// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 decodes a byte's two codes
+// exactly (low nibble first).
+__device__ __forceinline__ u32x4 dequant8_fp4(uint32_t q, uint32_t bcode, float tscale) {
+    const f32x2 sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)bcode, false);
+    const float s = sv.x;
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+    return u32x4{pack_bf16x2_canon((v0.x * s) * tscale, (v0.y * s) * tscale),
+                 pack_bf16x2_canon((v1.x * s) * tscale, (v1.y * s) * tscale),
+                 pack_bf16x2_canon((v2.x * s) * tscale, (v2.y * s) * tscale),
+                 pack_bf16x2_canon((v3.x * s) * tscale, (v3.y * s) * tscale)};
 }
 
 // ID of head h for token t, given its request (r, a) and the raw tokens
@@ -179,13 +173,16 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
     if (DTYPE == kFmtFP8) scale = g.scales[(int64_t)id * g.scale_stride];
     const float tscale = DTYPE == kFmtNVFP4 ? g.scales[0] : 0.f;
 
-    // chunks of 16 input bytes per row: D*2/16 for bf16, D/16 for fp8, D/32 for NVFP4
-    const int cpr = DTYPE == kFmtBF16 ? (g.dim >> 3) : (DTYPE == kFmtFP8 ? (g.dim >> 4) : (g.dim >> 5));
+    // Every lane produces one 16-byte output chunk (8 bf16 elements) per
+    // step, so stores are always lane-contiguous; its input is the same 8
+    // elements of the stored row: 16 bytes (bf16), 8 (fp8 codes) or 4 (NVFP4
+    // codes, plus the block's scale code).
+    const int cpr = g.dim >> 3;    // output chunks per row
     const int shift = g.cpr_log2;  // >= 0 when cpr is a power of two
     const int total = nrows * cpr;
     const char* __restrict__ table = (const char*)g.table;
-    const int64_t row_bytes =
-        DTYPE == kFmtBF16 ? (int64_t)g.dim * 2 : (DTYPE == kFmtFP8 ? (int64_t)g.dim : (int64_t)(g.dim >> 1));
+    constexpr int IB = DTYPE == kFmtBF16 ? 16 : (DTYPE == kFmtFP8 ? 8 : 4);  // input bytes per chunk
+    const int64_t row_bytes = (int64_t)cpr * IB;
     u32x4* __restrict__ out = (u32x4*)(g.rows + t0 * H * (int64_t)g.dim);
 
     for (int base = 0; base < total; base += kWave * UNROLL) {
@@ -201,34 +198,32 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
             if (DTYPE == kFmtFP8) sc[u] = __shfl(scale, row, kWave);
             if (idx < total) {
                 const int ch = idx - row * cpr;
-                const u32x4* src = (const u32x4*)(table + (int64_t)rid * row_bytes) + ch;
+                const char* src = table + (int64_t)rid * row_bytes + (int64_t)ch * IB;
+                if (DTYPE == kFmtBF16) {
 #if PLE_LOOKUP_NT_LOAD
-                v[u] = __builtin_nontemporal_load(src);
+                    v[u] = __builtin_nontemporal_load((const u32x4*)src);
 #else
-                v[u] = *src;
+                    v[u] = *(const u32x4*)src;
 #endif
-                // the two block-scale codes of this chunk's 32 elements
-                if (DTYPE == kFmtNVFP4)
-                    bsc[u] = *(const uint16_t*)(g.block_scales + (int64_t)rid * (g.dim >> 4) + 2 * ch);
+                } else if (DTYPE == kFmtFP8) {
+                    const u32x2 q = __builtin_nontemporal_load((const u32x2*)src);
+                    v[u] = u32x4{q.x, q.y, 0u, 0u};
+                } else {
+                    v[u] = u32x4{__builtin_nontemporal_load((const uint32_t*)src), 0u, 0u, 0u};
+                    bsc[u] = g.block_scales[(int64_t)rid * (g.dim >> 4) + (ch >> 1)];
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + u * kWave + lane;
             if (idx < total) {
-                if (DTYPE == kFmtBF16) {
+                if (DTYPE == kFmtBF16)
                     store16(out + idx, v[u]);
-                } else if (DTYPE == kFmtFP8) {
-                    u32x4 lo, hi;
-                    dequant16(v[u], sc[u], lo, hi);
-                    store16(out + 2 * idx, lo);
-                    store16(out + 2 * idx + 1, hi);
-                } else {
-                    u32x4 o[4];
-                    dequant32_fp4(v[u], bsc[u], tscale, o);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) store16(out + 4 * idx + k, o[k]);
-                }
+                else if (DTYPE == kFmtFP8)
+                    store16(out + idx, dequant8_fp8(v[u].x, v[u].y, sc[u]));
+                else
+                    store16(out + idx, dequant8_fp4(v[u].x, bsc[u], tscale));
             }
         }
     }
@@ -287,10 +282,15 @@ hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T,
     return hipGetLastError();
 }
 
-int lookup_tokens_per_wave(int H, int chunks_per_row) {
-    // about 16 sixteen-byte loads per lane, at most 64 rows (one lane per row for the IDs)
+static int lookup_loads(int dtype) {
+    return dtype == PLE_DTYPE_BF16 ? PLE_LOOKUP_LOADS : (dtype == PLE_DTYPE_NVFP4 ? PLE_LOOKUP_LOADS_FP4 : PLE_LOOKUP_LOADS_FP8);
+}
+
+int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype) {
+    // about lookup_loads(dtype) output chunks per lane, at most 64 rows (one
+    // lane per row for the IDs); chunks_per_row counts 16-byte output chunks
     const int chunks_per_token = H * chunks_per_row;
-    int tw = (PLE_LOOKUP_LOADS * kWave) / chunks_per_token;
+    int tw = (lookup_loads(dtype) * kWave) / chunks_per_token;
     if (tw > kWave / H) tw = kWave / H;
     return tw < 1 ? 1 : tw;
 }
@@ -298,10 +298,12 @@ int lookup_tokens_per_wave(int H, int chunks_per_row) {
 template <int DTYPE, int MODE>
 static hipError_t launch_lookup_t(const HashParams& hp, const LookupArgs& g, hipStream_t s) {
     constexpr int WPB = PLE_LOOKUP_BLOCK / kWave;  // waves per block
+    constexpr int UNROLL = DTYPE == kFmtBF16 ? PLE_LOOKUP_LOADS
+                                             : (DTYPE == kFmtNVFP4 ? PLE_LOOKUP_LOADS_FP4 : PLE_LOOKUP_LOADS_FP8);
     const int64_t waves = (g.num_tokens + g.tokens_per_wave - 1) / g.tokens_per_wave;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, PLE_LOOKUP_LOADS>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK),
-                       0, s, hp, g);
+    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK), 0, s, hp,
+                       g);
     return hipGetLastError();
 }
 

@@ -7,8 +7,10 @@ sizes are in SAMPLE).
 
 Workloads: the 8192-token prefill over an 8.39M-row bf16 table in HBM, the
 16384-token prefill over a 33.6M-row fp8 e4m3fn table with per-row scales,
-and the 8192-token prefill over a 67.1M-row (64 GiB) bf16 table in pinned
-host memory read directly by the GPU."""
+the 8192-token prefill over a 67.1M-row (64 GiB) bf16 table in pinned host
+memory read directly by the GPU, and the two table formats beyond the
+configurations: the fp8 codes with one global scale, and an NVFP4 table at the
+8k prefill's shape."""
 import numpy as np
 import pytest
 import torch
@@ -88,7 +90,37 @@ def test_prefill_16k_fp8_hbm_full():
     cfg = wl.CONFIGS[4]
     log("generating the 17.2 GB fp8 table")
     q_h, s_h = wl.make_table(cfg)
-    _prefill_full(cfg, dev(q_h), dev(s_h), q_h, s_h)
+    q_d = dev(q_h)
+    _prefill_full(cfg, q_d, dev(s_h), q_h, s_h)
+    # the same codes with one scale for the whole table, every token
+    g = np.asarray([s_h.max()], dtype=np.float32)
+    b = wl.make_batch(cfg, layers=2)
+    tb = ple.Table.from_tensor(q_d, dev(g))
+    rows = ple.ple_lookup(hash_params(b, 1), tb, dev(b.input_ids), dev(b.qsl))
+    want_ids = oracle_ids(b, 1)
+    np.testing.assert_array_equal(host_bits(rows), oracle.gather_fp8_global(q_h, g[0], want_ids).reshape(cfg.T, -1))
+    log("global-scale fp8 rows bit-exact on every token")
+
+
+def test_prefill_8k_nvfp4_hbm_full():
+    """The 8k prefill's batch over an NVFP4 table of the same 8.39M rows x 512."""
+    cfg = wl.CONFIGS[3]
+    log("generating the 2.4 GB NVFP4 table")
+    codes, bs, t = wl.make_nvfp4_table(cfg.num_rows, cfg.D, cfg.seed)
+    keep = (dev(codes), dev(bs), dev(np.asarray([t], dtype=np.float32)))
+    tb = ple.Table.nvfp4(*keep)
+    b = wl.make_batch(cfg, layers=2)
+    layer = 1
+    hp = hash_params(b, layer)
+    toks, qsl = dev(b.input_ids), dev(b.qsl)
+    rows = ple.ple_lookup(hp, tb, toks, qsl)
+    want_ids = oracle_ids(b, layer)
+    np.testing.assert_array_equal(host_bits(rows), oracle.gather_nvfp4(codes, bs, t, want_ids).reshape(cfg.T, -1))
+    log("NVFP4 rows bit-exact on every token")
+    kvw_h, cw_h, hidden_h = wl.make_kv_weight(cfg, layer=layer), wl.make_conv_weight(cfg), wl.make_hidden(cfg)
+    L = ple.Layer(hp, tb, dev_bf16(kvw_h), dev_bf16(cw_h), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    out = ple.ple_prefill_fused(L, toks, qsl, dev_bf16(hidden_h))
+    _check_chain(cfg, b, codes, (bs, t), layer, hidden_h, kvw_h, cw_h, host_bits(out))
 
 
 def test_prefill_8k_host_table_full():
