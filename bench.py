@@ -286,6 +286,12 @@ def bench_host_table(args):
     w_std = torch.from_numpy(wl.normal_bf16((4096, 4096), 78, 0.2).view(np.int16)).to(dev).view(torch.bfloat16)
     y_std = torch.empty((T, 4096), dtype=torch.bfloat16, device=dev)
     staging = [torch.empty((T, H * D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    # the distinct-rows prefetch: layers (only hash and table are read), workspace, distinct-row count
+    conv_dummy = torch.zeros((N, 4), dtype=torch.bfloat16, device=dev)
+    layers = [ple.Layer(hashes[l], tb, w_std, conv_dummy, conv_dilation=3) for l in range(L)]
+    ws_dd = [torch.empty((ple.ple_prefetch_dedup_workspace_bytes(T, H),), dtype=torch.uint8, device=dev)
+             for _ in range(2)]
+    n_unique = torch.zeros((L,), dtype=torch.int32, device=dev)
     side = ple.ple_stream_create_cu_masked(args.prefetch_cus)
     # the layer's work runs on a non-blocking stream: the legacy null stream
     # would serialise with the (blocking) side stream and hide the overlap
@@ -316,21 +322,32 @@ def bench_host_table(args):
             ple.ple_kv_proj(x_std, w_std, kv=y_std)
         sync_ms = timed(sync_layer, reps * L)
 
-        def pipelined(n_layers):
+        def fetch_plain(l, buf, stream):
+            ple.ple_lookup(hashes[l % L], tb, toks, qsl, rows=staging[buf], stream=stream)
+
+        def fetch_dedup(l, buf, stream):
+            ple.ple_prefetch_dedup(layers[l % L], toks, qsl, staging[buf], workspace=ws_dd[buf],
+                                   num_unique=n_unique[l % L:l % L + 1], stream=stream)
+
+        dedup_ms = timed(lambda i: fetch_dedup(i, 0, None), 2 * L)
+        torch.cuda.synchronize()
+        unique_frac = float(n_unique.float().mean().item()) / (T * H)
+
+        def pipelined(n_layers, fetch=fetch_plain):
             ready = [torch.cuda.Event() for _ in range(2)]
             free = [torch.cuda.Event() for _ in range(2)]
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             side.wait_event(e0)
-            ple.ple_lookup(hashes[0], tb, toks, qsl, rows=staging[0], stream=side)
+            fetch(0, 0, side)
             ready[0].record(side)
             for l in range(n_layers):
                 cur, nxt = l % 2, (l + 1) % 2
                 if l + 1 < n_layers:  # prefetch layer l+1 beside layer l
                     if l >= 1:
                         side.wait_event(free[nxt])
-                    ple.ple_lookup(hashes[(l + 1) % L], tb, toks, qsl, rows=staging[nxt], stream=side)
+                    fetch(l + 1, nxt, side)
                     ready[nxt].record(side)
                 main.wait_event(ready[cur])
                 ple.ple_kv_proj(x_std, w_std, kv=y_std)   # the layer's work (uses staging[cur] in a real model)
@@ -352,6 +369,8 @@ def bench_host_table(args):
         n_layers = reps * L
         pipelined(L)
         pipe_ms = min(pipelined(n_layers) for _ in range(3))
+        pipelined(L, fetch_dedup)
+        pipe_dd_ms = min(pipelined(n_layers, fetch_dedup) for _ in range(3))
         staged_ms = min(staged(n_layers) for _ in range(3))
     finally:
         torch.cuda.synchronize()
@@ -377,6 +396,12 @@ def bench_host_table(args):
         "staged_ms_per_layer": round(staged_ms / n_layers, 4),
         "exposed_lookup_ms_per_layer": round((pipe_ms - staged_ms) / n_layers, 4),
         "exposed_floor_ms_per_layer": round(max(0.0, lookup_ms - gemm_ms), 4),
+        "dedup": {"entry_point": "ple_prefetch_dedup", "distinct_rows_frac": round(unique_frac, 4),
+                  "host_bytes_per_layer": int(round(unique_frac * rows_bytes)),
+                  "lookup_ms_sync": round(dedup_ms, 4),
+                  "host_link_GBps": round(unique_frac * rows_bytes / (dedup_ms * 1e-3) / 1e9, 2),
+                  "pipelined_ms_per_layer": round(pipe_dd_ms / n_layers, 4),
+                  "exposed_lookup_ms_per_layer": round((pipe_dd_ms - staged_ms) / n_layers, 4)},
     }
     print(json.dumps(line), flush=True)
     hb.close()

@@ -187,6 +187,22 @@ int ple_lookup(const ple_hash_desc* hash, const ple_table_desc* table, const ple
 int ple_prefetch(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging, void* stream);
 
 /*
+ * The same staging rows with each distinct table row read once ([P1]
+ * 功能与动机: rows cross the host link; [P2] 功能与动机: that read is the
+ * time the prefetch hides).  Rows repeated within the batch are copied in
+ * device memory from their first read instead of crossing the host link
+ * again.  Same result as ple_prefetch, bit for bit.
+ * workspace: device memory of ple_prefetch_dedup_workspace_bytes(T, H) bytes,
+ * 256-byte aligned (IDs, a hash set and the repeat map; not read before being
+ * written).  num_unique: device int32 receiving the number of distinct rows
+ * (the rows read from the table), or NULL.  T*H at most 2^22
+ * (PLE_ERR_UNSUPPORTED beyond; the size function then returns 0).
+ */
+int ple_prefetch_dedup(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging,
+                       void* workspace, size_t workspace_bytes, int32_t* num_unique, void* stream);
+size_t ple_prefetch_dedup_workspace_bytes(int64_t max_tokens, int32_t num_heads);
+
+/*
  * Merged key/value projection ([P3] 实现拆解 item 1):
  *   kv[t][o] = bf16(sum_i x[t][i] * w[o][i]), fp32 accumulation, no bias.
  * x: device bf16 [T][K]; w: device bf16 [O][K]; kv: device bf16 [T][O].

@@ -27,6 +27,7 @@ from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_DTYPE_FP8_E4M3_GLOBAL
                    PLE_ERR_UNSUPPORTED, PLE_ERR_WORKSPACE, PLE_MAX_CONTEXT, PLE_MAX_HEADS, PLE_OK)
 
 __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_lookup", "ple_prefetch",
+           "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes",
            "ple_kv_proj", "ple_gate", "ple_conv", "ple_prefill_fused", "ple_prefill_workspace_bytes",
            "ple_host_alloc", "ple_host_free", "HostBuffer", "ple_stream_create_cu_masked", "ple_stream_destroy",
            "ple_error_message", "ple_version", "library"]
@@ -184,6 +185,26 @@ def ple_prefetch(layer: Layer, input_ids, query_start_loc, staging, *, ngram_con
     b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
     capi.check(capi.load().ple_prefetch(ctypes.byref(L), ctypes.byref(b), _ptr(staging), _stream(stream)),
                "ple_prefetch")
+    return staging
+
+
+def ple_prefetch_dedup_workspace_bytes(max_tokens: int, num_heads: int) -> int:
+    return int(capi.load().ple_prefetch_dedup_workspace_bytes(max_tokens, num_heads))
+
+
+def ple_prefetch_dedup(layer: Layer, input_ids, query_start_loc, staging, *, workspace=None, num_unique=None,
+                       ngram_context=None, ngram_context_out=None, stream=None):
+    """ple_prefetch reading each distinct table row once; num_unique (device int32 [1]) receives
+    the number of distinct rows."""
+    T = input_ids.shape[0]
+    need = ple_prefetch_dedup_workspace_bytes(T, layer.hash.num_heads)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=input_ids.device)
+    L = layer.desc()
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    capi.check(capi.load().ple_prefetch_dedup(ctypes.byref(L), ctypes.byref(b), _ptr(staging), _ptr(workspace),
+                                              workspace.numel(), _ptr(num_unique), _stream(stream)),
+               "ple_prefetch_dedup")
     return staging
 
 

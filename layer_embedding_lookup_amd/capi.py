@@ -60,6 +60,9 @@ _PROTOS = {
     "ple_lookup": (ctypes.c_int, [ctypes.POINTER(ple_hash_desc), ctypes.POINTER(ple_table_desc),
                                   ctypes.POINTER(ple_batch_desc), P, P, P]),
     "ple_prefetch": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P, P]),
+    "ple_prefetch_dedup": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P, P,
+                                          ctypes.c_size_t, P, P]),
+    "ple_prefetch_dedup_workspace_bytes": (ctypes.c_size_t, [I64, I32]),
     "ple_kv_proj": (ctypes.c_int, [P, P, I64, I32, I32, P, P]),
     "ple_gate": (ctypes.c_int, [P, P, I64, I32, ctypes.c_float, P, P, P]),
     "ple_conv": (ctypes.c_int, [P, ctypes.POINTER(ple_batch_desc), P, I32, I32, I32, P, P]),

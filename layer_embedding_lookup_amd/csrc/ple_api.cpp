@@ -367,6 +367,84 @@ int ple_prefetch(const ple_layer_desc* layer, const ple_batch_desc* batch, uint1
     return ple_lookup(&layer->hash, &layer->table, batch, nullptr, staging, stream);
 }
 
+namespace {
+constexpr int64_t kDedupMaxRows = (int64_t)1 << 22;
+
+// log2 of the hash-set capacity: a power of two >= 2 n (at least 256)
+int dedup_log2cap(int64_t n) {
+    int l = 8;
+    while (((int64_t)1 << l) < 2 * n) ++l;
+    return l;
+}
+}  // namespace
+
+size_t ple_prefetch_dedup_workspace_bytes(int64_t max_tokens, int32_t num_heads) {
+    if (max_tokens <= 0 || num_heads <= 0) return 0;
+    const int64_t n = max_tokens * num_heads;
+    if (n > kDedupMaxRows) return 0;
+    const size_t cap = (size_t)1 << dedup_log2cap(n);
+    return 2 * round256((size_t)n * 4) + 2 * round256(cap * 4);
+}
+
+int ple_prefetch_dedup(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging,
+                       void* workspace, size_t workspace_bytes, int32_t* num_unique, void* stream) {
+    if (layer == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
+    const ple_hash_desc* hash = &layer->hash;
+    const ple_table_desc* table = &layer->table;
+    HashParams hp;
+    int cpr_log2 = -1;
+    int rc = validate_hash(hash, &hp);
+    if (rc) return rc;
+    rc = validate_table(table, &cpr_log2);
+    if (rc) return rc;
+    rc = validate_heads_in_table(hash, table);
+    if (rc) return rc;
+    rc = validate_batch_tokens(batch);
+    if (rc) return rc;
+    const int64_t T = batch->num_tokens;
+    const int H = hash->num_heads;
+    const int64_t n = T * H;
+    if (n > kDedupMaxRows)
+        return fail(PLE_ERR_UNSUPPORTED, "dedup prefetch takes at most %lld rows (T*H = %lld)",
+                    (long long)kDedupMaxRows, (long long)n);
+    if (T > 0 && (staging == nullptr || !aligned16(staging)))
+        return fail(PLE_ERR_INVALID_ARGUMENT, "staging is NULL or not 16-byte aligned");
+    if (num_unique != nullptr && !aligned4(num_unique)) return fail(PLE_ERR_INVALID_ARGUMENT, "num_unique misaligned");
+    const size_t need = ple_prefetch_dedup_workspace_bytes(T, H);
+    if (T > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need))
+        return fail(PLE_ERR_WORKSPACE, "dedup workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    if (T == 0 && num_unique == nullptr && (batch->ngram_context_out == nullptr || batch->num_reqs == 0)) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (T > 0) {
+        const int l2 = dedup_log2cap(n);
+        char* ws = (char*)workspace;
+        int32_t* ids = (int32_t*)ws;
+        int32_t* slot_rep = (int32_t*)(ws + round256((size_t)n * 4));
+        int32_t* keys = (int32_t*)(ws + 2 * round256((size_t)n * 4));
+        int32_t* rep = (int32_t*)(ws + 2 * round256((size_t)n * 4) + round256(((size_t)1 << l2) * 4));
+        hipError_t e = launch_ngram_ids(hp, batch->input_ids, batch->query_start_loc, T, batch->num_reqs,
+                                        batch->ngram_context, ids, s);
+        if (e == hipSuccess) e = launch_dedup(ids, n, keys, rep, l2, slot_rep, num_unique, s);
+        if (e == hipSuccess) {
+            HashParams none;
+            memset(&none, 0, sizeof(none));
+            LookupArgs g = lookup_args(table, H, cpr_log2, nullptr, ids, T, nullptr, staging);
+            g.rep_of = slot_rep;
+            e = launch_lookup(none, g, table->dtype, kModeIds, s);
+        }
+        if (e == hipSuccess) e = launch_dedup_copy(slot_rep, n, table->dim, staging, s);
+        if (e != hipSuccess) return hip_fail(e, "dedup prefetch launch");
+    } else if (num_unique != nullptr) {
+        hipError_t e = launch_dedup(nullptr, 0, nullptr, nullptr, 8, nullptr, num_unique, s);
+        if (e != hipSuccess) return hip_fail(e, "dedup prefetch launch");
+    }
+    rc = run_context_out(hash, batch, s);
+    return rc ? rc : ok();
+}
+
 int ple_kv_proj(const uint16_t* x, const uint16_t* w, int64_t num_tokens, int32_t k_dim, int32_t out_dim,
                 uint16_t* kv, void* stream) {
     int rc = validate_gemm(x, w, num_tokens, k_dim, out_dim, kv);

@@ -12,6 +12,7 @@ struct LookupArgs {
     const int32_t* qsl;
     const int32_t* ctx;
     const int32_t* ids_in;
+    const int32_t* rep_of;  // ids mode, optional: position i is gathered only when rep_of[i] == i
     int32_t* ids_out;
     const void* table;
     const float* scales;          // fp8: per-row scales (scale_stride 1) or one scale (0); NVFP4: one scale
@@ -36,6 +37,10 @@ hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T,
                               const int32_t* ctx, int32_t* ctx_out, hipStream_t s);
 int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype);
 hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s);
+
+hipError_t launch_dedup(const int32_t* ids, int64_t n, int32_t* keys, int32_t* rep, int log2cap,
+                        int32_t* slot_rep, int32_t* num_unique, hipStream_t s);
+hipError_t launch_dedup_copy(const int32_t* rep_of, int64_t n, int dim, uint16_t* rows, hipStream_t s);
 
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s);

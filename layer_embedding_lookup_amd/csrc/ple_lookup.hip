@@ -169,6 +169,9 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
         id = active ? g.ids_in[t0 * H + lane] : 0;
         id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
     }
+    // ids mode with rep_of: a repeated row is left for a later copy
+    int skip = 0;
+    if (MODE == kModeIds && g.rep_of != nullptr && active) skip = g.rep_of[t0 * H + lane] != (int32_t)(t0 * H + lane);
     float scale = 0.f;
     if (DTYPE == kFmtFP8) scale = g.scales[(int64_t)id * g.scale_stride];
     const float tscale = DTYPE == kFmtNVFP4 ? g.scales[0] : 0.f;
@@ -196,7 +199,8 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
             row = row < nrows ? row : nrows - 1;
             const int rid = __shfl(id, row, kWave);
             if (DTYPE == kFmtFP8) sc[u] = __shfl(scale, row, kWave);
-            if (idx < total) {
+            const int rskip = MODE == kModeIds ? __shfl(skip, row, kWave) : 0;
+            if (idx < total && !rskip) {
                 const int ch = idx - row * cpr;
                 const char* src = table + (int64_t)rid * row_bytes + (int64_t)ch * IB;
                 if (DTYPE == kFmtBF16) {
@@ -217,7 +221,12 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + u * kWave + lane;
-            if (idx < total) {
+            int rskip = 0;
+            if (MODE == kModeIds) {
+                int row = shift >= 0 ? (idx >> shift) : (idx / cpr);
+                rskip = __shfl(skip, row < nrows ? row : nrows - 1, kWave);
+            }
+            if (idx < total && !rskip) {
                 if (DTYPE == kFmtBF16)
                     store16(out + idx, v[u]);
                 else if (DTYPE == kFmtFP8)

@@ -21,7 +21,7 @@ FAKE = 1 << 40  # a 256-aligned address that is never dereferenced: every call b
 
 def test_exports_every_header_function():
     names = capi.header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(capi._PROTOS)
@@ -40,8 +40,8 @@ def _hash(H=4, hpn=2, C=2, first=0, V=None, off=None):
     return capi.ple_hash_desc(H, hpn, C, first, 0, 0, m.ctypes.data, V.ctypes.data, off.ctypes.data), keep
 
 
-def _table(rows=420, dim=32, dtype=capi.PLE_DTYPE_BF16, ptr=FAKE, scales=None):
-    return capi.ple_table_desc(ptr, rows, dim, dtype, scales)
+def _table(rows=420, dim=32, dtype=capi.PLE_DTYPE_BF16, ptr=FAKE, scales=None, block_scales=None):
+    return capi.ple_table_desc(ptr, rows, dim, dtype, scales, block_scales)
 
 
 def _batch(T=8, R=2, ctx=None, ctx_out=None, state=None, state_out=None):
@@ -161,3 +161,32 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(capi, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         capi.load()
+
+
+def test_table_formats_rejected_before_any_launch():
+    h, keep = _hash()
+    b = _batch()
+    for t, code, text in [
+            (_table(dtype=capi.PLE_DTYPE_FP8_E4M3_GLOBAL), E_ARG, "row_scales"),
+            (_table(dtype=capi.PLE_DTYPE_NVFP4, scales=FAKE), E_ARG, "block_scales"),
+            (_table(dtype=capi.PLE_DTYPE_NVFP4, dim=48, scales=FAKE, block_scales=FAKE), E_UNSUP, "16 bytes"),
+            (_table(dtype=capi.PLE_DTYPE_NVFP4, scales=FAKE, block_scales=FAKE + 1), E_ARG, "2-byte"),
+            (_table(dtype=7), E_UNSUP, "PLE_DTYPE")]:
+        assert lib.ple_lookup(ctypes.byref(h), ctypes.byref(t), ctypes.byref(b), None, FAKE, None) == code
+        assert text in _msg()
+
+
+def test_dedup_workspace_size_and_limits():
+    f = lib.ple_prefetch_dedup_workspace_bytes
+    # T*H = 24*4 = 96 rows: IDs and repeat map 96*4 bytes each (256-rounded), hash set of 256 slots x 2
+    assert f(24, 4) == 2 * 512 + 2 * 1024
+    assert f(8192, 8) == 2 * 65536 * 4 + 2 * 131072 * 4
+    assert f(0, 8) == 0 and f(1 << 22, 2) == 0  # beyond 2^22 rows: unsupported
+    h, keep = _hash()
+    layer = capi.ple_layer_desc(h, _table(), FAKE, 128, 1e-6, FAKE, 4, 2)
+    b = _batch()
+    assert lib.ple_prefetch_dedup(ctypes.byref(layer), ctypes.byref(b), FAKE, FAKE, 16, None, None) == E_WS
+    assert lib.ple_prefetch_dedup(ctypes.byref(layer), ctypes.byref(b), FAKE, FAKE + 4, 1 << 20, None, None) == E_WS
+    big = capi.ple_batch_desc(FAKE, FAKE, 1 << 21, 2, 0, None, None, None, None)
+    assert lib.ple_prefetch_dedup(ctypes.byref(layer), ctypes.byref(big), FAKE, FAKE, 1 << 30, None, None) == E_UNSUP
+    assert lib.ple_prefetch_dedup(None, ctypes.byref(b), FAKE, FAKE, 1 << 20, None, None) == E_ARG

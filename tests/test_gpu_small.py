@@ -566,3 +566,44 @@ def test_lookup_nvfp4_and_fused_prefill():
                                 ngram_context=dev(b.ngram_context), conv_state=dev_bf16(b.conv_state))
     ref = _oracle_chain(cfg, b, codes, (bs, t), kvw, cw, hidden)
     assert np.abs(bf16_f64(host_bits(out)) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
+
+
+# ------------------------------------------------------------------ dedup prefetch
+
+@pytest.mark.parametrize("variant", ["cfg1", "cfg2", "cfg1-nvfp4", "repeats"])
+def test_prefetch_dedup_equals_prefetch(variant):
+    cfg = wl.CONFIGS[2 if variant == "cfg2" else 1]
+    b = wl.make_batch(cfg, with_context=(variant != "repeats"))
+    toks = b.input_ids.copy()
+    if variant == "repeats":  # every token the same: only the first positions differ (EOS windows)
+        toks[:] = 77
+    if variant == "cfg1-nvfp4":
+        codes, bs, t = wl.make_nvfp4_table(cfg.num_rows, cfg.D, cfg.seed)
+        tb, keep = _nvfp4_dev(codes, bs, t)
+        L = ple.Layer(hash_params(b), tb, dev_bf16(wl.make_kv_weight(cfg)), dev_bf16(wl.make_conv_weight(cfg)),
+                      conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    else:
+        L, table, scales, kvw, cw, keep = _layer(cfg, b)
+    ctx = None if b.ngram_context is None else dev(b.ngram_context)
+    d_toks, d_qsl = dev(toks), dev(b.qsl)
+    plain = torch.empty((cfg.T, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+    ple.ple_prefetch(L, d_toks, d_qsl, plain, ngram_context=ctx)
+    staging = torch.full_like(plain, float("nan"))
+    nu = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    ple.ple_prefetch_dedup(L, d_toks, d_qsl, staging, num_unique=nu, ngram_context=ctx)
+    assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
+    ids = oracle.ngram_ids(toks, b.qsl, b.multipliers[0], b.vocab_sizes, b.offsets, context_len=cfg.context_len,
+                           heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS, ngram_context=b.ngram_context)
+    assert int(nu.item()) == len(np.unique(ids))
+    if variant == "repeats":
+        assert int(nu.item()) < ids.size // 2
+
+
+def test_prefetch_dedup_empty_batch_counts_zero():
+    cfg = wl.CONFIGS[1]
+    b = wl.make_batch(cfg)
+    L, table, scales, kvw, cw, keep = _layer(cfg, b)
+    nu = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+    staging = torch.empty((1, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+    ple.ple_prefetch_dedup(L, dev(np.zeros(0, np.int32)), dev(np.zeros(1, np.int32)), staging, num_unique=nu)
+    assert int(nu.item()) == 0

@@ -165,6 +165,15 @@ def test_prefill_8k_host_table_full():
         finally:
             ple.ple_stream_destroy(side)
         _check_chain(cfg, b, table_h, None, layer, hidden_h, kvw_h, cw_h, host_bits(out))
+        # distinct rows only across the host link: the same staging, bit for bit
+        staging2 = torch.empty_like(staging)
+        nu = torch.zeros((1,), dtype=torch.int32, device=DEV)
+        ple.ple_prefetch_dedup(L, toks, qsl, staging2, num_unique=nu)
+        torch.cuda.synchronize()
+        assert torch.equal(staging2.view(torch.int16), staging.view(torch.int16))
+        n_unique = len(np.unique(oracle_ids(b, layer)))
+        assert int(nu.item()) == n_unique
+        log(f"dedup prefetch bit-exact; {n_unique} of {cfg.T * cfg.H} rows distinct")
     finally:
         torch.cuda.synchronize()
         hb.close()
