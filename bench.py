@@ -46,7 +46,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="prefill-8k-bf16-hbm",
                     choices=["prefill-8k-bf16-hbm", "prefill-16k-fp8-hbm", "prefill-16k-fp8global-hbm",
-                             "prefill-8k-nvfp4-hbm", "prefill-8k-bf16-host"],
+                             "prefill-8k-nvfp4-hbm", "prefill-8k-bf16-host", "select-rows-8k"],
                     help="the default is the benchmark line; the others report the fp8-table (per-row or "
                          "one global scale), NVFP4-table and host-resident-table variants")
     args = ap.parse_args()
@@ -65,6 +65,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.workload == "prefill-8k-bf16-host":
         return bench_host_table(args)
+    if args.workload == "select-rows-8k":
+        return bench_select_rows(args)
     # table format of the workload; the batch, projection and conv are those of
     # the 8k prefill (bf16, NVFP4) or the 16k prefill (fp8 tables)
     fmt = {"prefill-8k-bf16-hbm": "bf16", "prefill-16k-fp8-hbm": "fp8", "prefill-16k-fp8global-hbm": "fp8-global",
@@ -405,6 +407,43 @@ def bench_host_table(args):
     }
     print(json.dumps(line), flush=True)
     hb.close()
+    return 0
+
+
+def bench_select_rows(args):
+    """One-GPU part of a table sharded over 8 data-parallel replicas at the 8k
+    prefill's width: the rank-major gathered buffer [8][8 x 8192][512] bf16
+    (each shard's 1 of 8 heads for every replica's 8192-token slot), and one
+    replica selecting its 8192 tokens x 4096 (all heads)."""
+    import torch
+
+    import layer_embedding_lookup_amd as ple
+
+    dev = "cuda:0"
+    E, S, W = 8, 8192, 512
+    gathered = torch.randn((E, E * S, W), device=dev).to(torch.bfloat16)
+    out = torch.empty((S, E * W), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for r in range(E):
+        ple.ple_select_rows(gathered, r, S, out=out)
+    ms = min(timed(lambda i: ple.ple_select_rows(gathered, i % E, S, out=out), 64) for _ in range(3))
+    nbytes = 2 * S * E * W * 2
+    line = {"metric": "GB/s, rank-major row select (one-GPU part of a DP-sharded table), 8k-token prefill width",
+            "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": 64,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "select-rows-8k", "shards": E, "slot_tokens": S, "shard_width": W},
+            "ms": round(ms, 5), "bytes": nbytes, "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps(line), flush=True)
     return 0
 
 

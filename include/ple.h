@@ -270,6 +270,43 @@ int ple_host_free(void* host);
 int ple_stream_create_cu_masked(int32_t num_cus, void** stream);
 int ple_stream_destroy(void* stream);
 
+/*
+ * The one-GPU part of a table sharded across data-parallel replicas ([P1]
+ * 实现拆解 item 3 and 关键源码片段 _get_dp_gather_slot: IDs of every replica
+ * gathered into equal padded slots, then each replica selects its own token
+ * window; [P2] 实现拆解 items 3-4: heads sharded in TP-major order so the
+ * gathered shards concatenate in head order, and a kernel that takes a
+ * rank's token window out of the rank-major gathered buffer).  The
+ * collectives themselves are the caller's.
+ *
+ * ple_dp_gather_slot: slot = max(token_counts[g0 .. g0+group_size)) and
+ * offset = (dp_rank - g0) * slot for the group g0 = dp_rank - dp_rank % group_size
+ * that contains dp_rank (group_size 1: slot = token_counts[dp_rank], offset 0).
+ * Host-only, synchronous.  token_counts: host [dp_size].
+ */
+int ple_dp_gather_slot(const int64_t* token_counts, int32_t dp_size, int32_t group_size, int32_t dp_rank,
+                       int64_t* slot, int64_t* offset);
+
+/*
+ * ple_head_shard: heads of shard s = tp_rank * dp_size + dp_rank (TP-major)
+ * out of num_heads split evenly over tp_size * dp_size shards:
+ * [s * num_heads / shards, (s + 1) * num_heads / shards).  An uneven split
+ * or an empty shard is rejected (PLE_ERR_UNSUPPORTED).  Host-only.
+ */
+int ple_head_shard(int32_t num_heads, int32_t tp_size, int32_t tp_rank, int32_t dp_size, int32_t dp_rank,
+                   int32_t* first_head, int32_t* shard_heads);
+
+/*
+ * ple_select_rows: this rank's token window out of a rank-major gathered
+ * buffer: gathered is device bf16 [num_shards][num_shards * slot][width]
+ * (shard k's lookup of every rank's padded slot, rank r's tokens at rows
+ * r*slot .. r*slot+slot-1); out is device bf16 [num_tokens][num_shards * width]
+ * with out[t][k*width + c] = gathered[k][rank*slot + t][c] for
+ * t < num_tokens <= slot.  width a multiple of 8; 16-byte aligned pointers.
+ */
+int ple_select_rows(const uint16_t* gathered, int32_t num_shards, int64_t slot, int32_t rank, int64_t num_tokens,
+                    int32_t width, uint16_t* out, void* stream);
+
 /* Message for the last failure on the calling thread ("" if none). */
 const char* ple_error_message(void);
 /* Library version string. */

@@ -27,7 +27,8 @@ from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_DTYPE_FP8_E4M3_GLOBAL
                    PLE_ERR_UNSUPPORTED, PLE_ERR_WORKSPACE, PLE_MAX_CONTEXT, PLE_MAX_HEADS, PLE_OK)
 
 __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_lookup", "ple_prefetch",
-           "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes",
+           "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes", "ple_dp_gather_slot", "ple_head_shard",
+           "ple_select_rows",
            "ple_kv_proj", "ple_gate", "ple_conv", "ple_prefill_fused", "ple_prefill_workspace_bytes",
            "ple_host_alloc", "ple_host_free", "HostBuffer", "ple_stream_create_cu_masked", "ple_stream_destroy",
            "ple_error_message", "ple_version", "library"]
@@ -206,6 +207,34 @@ def ple_prefetch_dedup(layer: Layer, input_ids, query_start_loc, staging, *, wor
                                               workspace.numel(), _ptr(num_unique), _stream(stream)),
                "ple_prefetch_dedup")
     return staging
+
+
+def ple_dp_gather_slot(token_counts, group_size: int, dp_rank: int) -> tuple[int, int]:
+    """(slot, offset) of dp_rank's tokens in its group's padded, rank-major gathered buffer."""
+    c = np.ascontiguousarray(token_counts, dtype=np.int64)
+    slot, off = ctypes.c_int64(), ctypes.c_int64()
+    capi.check(capi.load().ple_dp_gather_slot(c.ctypes.data, len(c), group_size, dp_rank, ctypes.byref(slot),
+                                              ctypes.byref(off)), "ple_dp_gather_slot")
+    return slot.value, off.value
+
+
+def ple_head_shard(num_heads: int, tp_size: int, tp_rank: int, dp_size: int, dp_rank: int) -> tuple[int, int]:
+    """(first_head, shard_heads) of the TP-major head shard of (tp_rank, dp_rank)."""
+    f, n = ctypes.c_int32(), ctypes.c_int32()
+    capi.check(capi.load().ple_head_shard(num_heads, tp_size, tp_rank, dp_size, dp_rank, ctypes.byref(f),
+                                          ctypes.byref(n)), "ple_head_shard")
+    return f.value, n.value
+
+
+def ple_select_rows(gathered, rank: int, num_tokens: int, *, out=None, stream=None):
+    """gathered bf16 [E][E*slot][W] -> out bf16 [num_tokens][E*W] (rank's token window, shards in order)."""
+    E, rows, W = gathered.shape
+    slot = rows // E
+    if out is None:
+        out = torch.empty((num_tokens, E * W), dtype=torch.bfloat16, device=gathered.device)
+    capi.check(capi.load().ple_select_rows(_ptr(gathered), E, slot, rank, num_tokens, W, _ptr(out),
+                                           _stream(stream)), "ple_select_rows")
+    return out
 
 
 def ple_kv_proj(x, w, *, kv=None, stream=None):

@@ -445,6 +445,63 @@ int ple_prefetch_dedup(const ple_layer_desc* layer, const ple_batch_desc* batch,
     return rc ? rc : ok();
 }
 
+int ple_dp_gather_slot(const int64_t* token_counts, int32_t dp_size, int32_t group_size, int32_t dp_rank,
+                       int64_t* slot, int64_t* offset) {
+    if (token_counts == nullptr || slot == nullptr || offset == nullptr)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "dp_gather_slot pointers must be non-NULL");
+    if (dp_size < 1 || group_size < 1 || dp_size % group_size != 0)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "group size %d must divide dp size %d", group_size, dp_size);
+    if (dp_rank < 0 || dp_rank >= dp_size) return fail(PLE_ERR_INVALID_ARGUMENT, "dp rank %d outside 0..%d", dp_rank, dp_size - 1);
+    const int32_t g0 = dp_rank - dp_rank % group_size;
+    int64_t mx = 0;
+    for (int32_t r = g0; r < g0 + group_size; ++r) {
+        if (token_counts[r] < 0) return fail(PLE_ERR_INVALID_ARGUMENT, "negative token count at rank %d", r);
+        mx = token_counts[r] > mx ? token_counts[r] : mx;
+    }
+    *slot = mx;
+    *offset = (int64_t)(dp_rank - g0) * mx;
+    return ok();
+}
+
+int ple_head_shard(int32_t num_heads, int32_t tp_size, int32_t tp_rank, int32_t dp_size, int32_t dp_rank,
+                   int32_t* first_head, int32_t* shard_heads) {
+    if (first_head == nullptr || shard_heads == nullptr)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "head_shard outputs must be non-NULL");
+    if (tp_size < 1 || dp_size < 1 || tp_rank < 0 || tp_rank >= tp_size || dp_rank < 0 || dp_rank >= dp_size)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "tp/dp ranks outside their sizes");
+    if (num_heads < 1 || num_heads > PLE_MAX_HEADS)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "num_heads %d outside 1..%d", num_heads, PLE_MAX_HEADS);
+    const int64_t shards = (int64_t)tp_size * dp_size;
+    if (num_heads % shards != 0)
+        return fail(PLE_ERR_UNSUPPORTED, "%d heads do not split evenly over %lld shards (an empty or uneven head shard)",
+                    num_heads, (long long)shards);
+    const int32_t per = (int32_t)(num_heads / shards);
+    const int32_t s = tp_rank * dp_size + dp_rank;  // TP-major
+    *first_head = s * per;
+    *shard_heads = per;
+    return ok();
+}
+
+int ple_select_rows(const uint16_t* gathered, int32_t num_shards, int64_t slot, int32_t rank, int64_t num_tokens,
+                    int32_t width, uint16_t* out, void* stream) {
+    if (num_shards < 1 || num_shards > 1024) return fail(PLE_ERR_INVALID_ARGUMENT, "num_shards %d outside 1..1024", num_shards);
+    if (rank < 0 || rank >= num_shards) return fail(PLE_ERR_INVALID_ARGUMENT, "rank %d outside 0..%d", rank, num_shards - 1);
+    if (slot < 0 || num_tokens < 0 || num_tokens > slot)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens %lld must lie in 0..slot %lld", (long long)num_tokens,
+                    (long long)slot);
+    if (width < 8 || width % 8 != 0) return fail(PLE_ERR_UNSUPPORTED, "width %d is not a positive multiple of 8", width);
+    if ((int64_t)num_shards * slot > PLE_MAX_TOKENS * (int64_t)64)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "gathered buffer of %lld rows per shard is too large",
+                    (long long)((int64_t)num_shards * slot));
+    if (num_tokens == 0) return ok();
+    if (gathered == nullptr || out == nullptr || !aligned16(gathered) || !aligned16(out))
+        return fail(PLE_ERR_INVALID_ARGUMENT, "gathered and out must be non-NULL and 16-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_select_rows(gathered, num_shards, slot, rank, num_tokens, width, out, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "select_rows launch");
+}
+
 int ple_kv_proj(const uint16_t* x, const uint16_t* w, int64_t num_tokens, int32_t k_dim, int32_t out_dim,
                 uint16_t* kv, void* stream) {
     int rc = validate_gemm(x, w, num_tokens, k_dim, out_dim, kv);

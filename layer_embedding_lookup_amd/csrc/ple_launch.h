@@ -42,6 +42,9 @@ hipError_t launch_dedup(const int32_t* ids, int64_t n, int32_t* keys, int32_t* r
                         int32_t* slot_rep, int32_t* num_unique, hipStream_t s);
 hipError_t launch_dedup_copy(const int32_t* rep_of, int64_t n, int dim, uint16_t* rows, hipStream_t s);
 
+hipError_t launch_select_rows(const uint16_t* gathered, int E, int64_t slot, int rank, int64_t n, int width,
+                              uint16_t* out, hipStream_t s);
+
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s);
 

@@ -47,6 +47,7 @@ def _lib():
     lib.orc_gather_fp8.argtypes = [P, P, I32, P, I64, P]
     lib.orc_gather_fp8_global.argtypes = [P, ctypes.c_float, I32, P, I64, P]
     lib.orc_gather_nvfp4.argtypes = [P, P, ctypes.c_float, I32, P, I64, P]
+    lib.orc_select_rows.argtypes = [P, I32, I64, I32, I64, I32, P]
     lib.orc_e2m1_value.argtypes = [ctypes.c_uint8]
     lib.orc_e2m1_value.restype = D
     lib.orc_e4m3fn_value.argtypes = [ctypes.c_uint8]
@@ -131,6 +132,41 @@ def gather_nvfp4(codes, block_scales, tensor_scale, ids):
     rows = np.empty((ids.shape[0], D), dtype=np.uint16)
     _lib().orc_gather_nvfp4(_p(codes), _p(bs), float(np.float32(tensor_scale)), D, _p(ids), ids.shape[0], _p(rows))
     return rows
+
+
+def dp_gather_slot(token_counts, group_size, dp_rank):
+    """[P1] 关键源码片段 _get_dp_gather_slot: a group of group_size consecutive DP
+    ranks gathers its IDs into slots of the group's largest token count; a
+    rank's tokens start at (its rank within the group) * slot.  (The page
+    takes the rank in the whole DP group; with one group spanning the DP group
+    the two agree.)  group_size 1: (own count, 0)."""
+    counts = [int(c) for c in token_counts]
+    if group_size == 1:
+        return counts[dp_rank], 0
+    g0 = (dp_rank // group_size) * group_size
+    slot = max(counts[g0:g0 + group_size])
+    return slot, (dp_rank - g0) * slot
+
+
+def head_shard(num_heads, tp_size, tp_rank, dp_size, dp_rank):
+    """[P2] 实现拆解 item 3 (engram_head_shard_rank, TP-major): shard index
+    tp_rank * dp_size + dp_rank, heads split evenly; uneven or empty shards
+    are rejected (None)."""
+    shards = tp_size * dp_size
+    if num_heads % shards != 0 or num_heads // shards == 0:
+        return None
+    per = num_heads // shards
+    s = tp_rank * dp_size + dp_rank
+    return s * per, per
+
+
+def select_rows(gathered, rank, n):
+    """gathered uint16 [E][E*slot][W] -> [n][E*W] (see orc_select_rows)."""
+    g = _c(gathered, np.uint16)
+    E, rows, W = g.shape
+    out = np.empty((n, E * W), dtype=np.uint16)
+    _lib().orc_select_rows(_p(g), E, rows // E, rank, n, W, _p(out))
+    return out
 
 
 def e2m1_value(code: int) -> float:

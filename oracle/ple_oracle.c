@@ -205,6 +205,15 @@ void orc_gather_nvfp4(const uint8_t* codes, const uint8_t* block_scales, float t
     }
 }
 
+void orc_select_rows(const uint16_t* gathered, int32_t num_shards, int64_t slot, int32_t rank, int64_t n,
+                     int32_t width, uint16_t* out) {
+    for (int64_t t = 0; t < n; ++t)
+        for (int32_t k = 0; k < num_shards; ++k)
+            for (int32_t c = 0; c < width; ++c)
+                out[(t * num_shards + k) * width + c] =
+                    gathered[((int64_t)k * num_shards * slot + (int64_t)rank * slot + t) * width + c];
+}
+
 /* ------------------------------------------------------------------------ */
 /* merged key/value projection                                               */
 /* ------------------------------------------------------------------------ */

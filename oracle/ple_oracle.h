@@ -85,6 +85,13 @@ void orc_gather_nvfp4(const uint8_t* codes, const uint8_t* block_scales, float t
 uint16_t orc_bf16_from_double(double x);
 double orc_bf16_value(uint16_t bits);
 
+/* Rank-major row selection ([P1] 实现拆解 item 3, selecting a replica's token
+ * window after the gather; [P2] 实现拆解 item 4, the rank-major select-rows
+ * kernel): out[t][k*width + c] = gathered[k][rank*slot + t][c] for t < n,
+ * gathered [E][E*slot][width], out [n][E*width]; a bit copy. */
+void orc_select_rows(const uint16_t* gathered, int32_t num_shards, int64_t slot, int32_t rank, int64_t n,
+                     int32_t width, uint16_t* out);
+
 /* kv[t][o] = bf16(sum_k x[t][k] * w[o][k]) with the sum in double ([P3] merged kv_proj). */
 void orc_kv_proj(const uint16_t* x, const uint16_t* w, int64_t num_tokens, int32_t k_dim, int32_t out_dim,
                  uint16_t* kv);

@@ -607,3 +607,53 @@ def test_prefetch_dedup_empty_batch_counts_zero():
     staging = torch.empty((1, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
     ple.ple_prefetch_dedup(L, dev(np.zeros(0, np.int32)), dev(np.zeros(1, np.int32)), staging, num_unique=nu)
     assert int(nu.item()) == 0
+
+
+# ------------------------------------------------------------------ data-parallel shards (one GPU)
+
+@pytest.mark.parametrize("E,W,counts", [(1, 8, [37]), (2, 512, [300, 123]), (4, 2048, [17, 0, 64, 5]),
+                                        (3, 96, [1000, 999, 1])])
+def test_select_rows_parity(E, W, counts):
+    rng = np.random.default_rng(E * 100 + W)
+    S = max(counts)
+    gathered = rng.integers(0, 65536, size=(E, E * S, W), dtype=np.uint16)
+    g = dev_bf16(gathered)
+    for r in range(E):
+        out = ple.ple_select_rows(g, r, counts[r])
+        np.testing.assert_array_equal(host_bits(out), oracle.select_rows(gathered, r, counts[r]))
+
+
+def test_sharded_lookup_equals_unsharded():
+    """The whole one-GPU data flow of a table sharded over E replicas: each
+    replica's batch padded into a slot, each head shard looked up over every
+    slot, the shards stacked (the all-gather), and each replica's window
+    selected: the same rows as the replica's own unsharded lookup."""
+    cfg = wl.CONFIGS[2]
+    E = 4
+    b = wl.make_batch(cfg)
+    table_h, _ = wl.make_table(cfg)
+    tb = ple.Table.from_tensor(dev_bf16(table_h))
+    # split the 256 one-token requests into E replicas of uneven sizes
+    cuts = [0, 40, 130, 131, 256]
+    counts = [cuts[r + 1] - cuts[r] for r in range(E)]
+    slot, _ = ple.ple_dp_gather_slot(counts, E, 0)
+    toks = np.full(E * slot, wl.EOS, dtype=np.int32)
+    ctx = np.full((E * slot, cfg.context_len), wl.EOS, dtype=np.int32)
+    for r in range(E):
+        s0, off = cuts[r], ple.ple_dp_gather_slot(counts, E, r)[1]
+        toks[off:off + counts[r]] = b.input_ids[s0:s0 + counts[r]]
+        ctx[off:off + counts[r]] = b.ngram_context[s0:s0 + counts[r]]
+    qsl = np.arange(E * slot + 1, dtype=np.int32)  # every slot position its own one-token request
+    shards = []
+    for k in range(E):
+        first, per = ple.ple_head_shard(cfg.H, 1, 0, E, k)
+        hp = hash_params(b, first_head=first, num_heads=per)
+        shards.append(ple.ple_lookup(hp, tb, dev(toks), dev(qsl), ngram_context=dev(ctx)))
+    gathered = torch.stack(shards)  # [E][E*slot][per*D]
+    for r in range(E):
+        s0 = cuts[r]
+        mine = ple.ple_select_rows(gathered, r, counts[r])
+        qr = np.arange(counts[r] + 1, dtype=np.int32)
+        full = ple.ple_lookup(hash_params(b), tb, dev(b.input_ids[s0:s0 + counts[r]]), dev(qr),
+                              ngram_context=dev(b.ngram_context[s0:s0 + counts[r]]))
+        assert torch.equal(mine.view(torch.int16), full.view(torch.int16)), r
