@@ -46,7 +46,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="prefill-8k-bf16-hbm",
                     choices=["prefill-8k-bf16-hbm", "prefill-16k-fp8-hbm", "prefill-16k-fp8global-hbm",
-                             "prefill-8k-nvfp4-hbm", "prefill-8k-bf16-host", "select-rows-8k"],
+                             "prefill-8k-nvfp4-hbm", "prefill-8k-bf16-host", "select-rows-8k",
+                             "spec-decode-256x4"],
                     help="the default is the benchmark line; the others report the fp8-table (per-row or "
                          "one global scale), NVFP4-table and host-resident-table variants")
     args = ap.parse_args()
@@ -67,6 +68,8 @@ def main() -> int:
         return bench_host_table(args)
     if args.workload == "select-rows-8k":
         return bench_select_rows(args)
+    if args.workload == "spec-decode-256x4":
+        return bench_spec_decode(args)
     # table format of the workload; the batch, projection and conv are those of
     # the 8k prefill (bf16, NVFP4) or the 16k prefill (fp8 tables)
     fmt = {"prefill-8k-bf16-hbm": "bf16", "prefill-16k-fp8-hbm": "fp8", "prefill-16k-fp8global-hbm": "fp8-global",
@@ -443,6 +446,147 @@ def bench_select_rows(args):
             "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "select-rows-8k", "shards": E, "slot_tokens": S, "shard_width": W},
             "ms": round(ms, 5), "bytes": nbytes, "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_spec_decode(args):
+    """Speculative decode on the decode-shaped model (256 requests, 8 heads over
+    a ~1M x 256 bf16 table, hidden 2048, conv 4 / dilation 3): each request
+    verifies a 4-token window (its last token and 3 drafts) through the fused
+    path, then the carried conv state and n-gram context are committed for the
+    1..4 accepted tokens (uniform).  A step is one layer's verify + commit,
+    timed as a replayed HIP graph (the eager loop's time is reported beside
+    it); verify and commit are each timed as graphs of back-to-back calls."""
+    import numpy as np
+    import torch
+
+    import layer_embedding_lookup_amd as ple
+    import workloads as wl
+
+    dev = "cuda:0"
+    cfg = wl.CONFIGS[2]
+    W, L = 4, args.layers
+    R = cfg.T
+    T = R * W
+    b = wl.make_batch(cfg, layers=L)
+    toks_h = wl.make_tokens(cfg, T=T)
+    qsl_h = np.arange(0, T + 1, W, dtype=np.int32)
+    acc_h = wl.uniform_ints(wl.stream_seed(cfg.seed, 99), R, 1, W + 1)
+    log(f"spec decode: R={R} window={W} T={T} rows={cfg.num_rows} D={cfg.D} N={cfg.N}")
+    table_h, _ = wl.make_table(cfg)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def it(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    tb = ple.Table.from_tensor(bf(table_h))
+    kv_ws = [bf(wl.make_kv_weight(cfg, layer=i)) for i in range(4)]
+    conv_w = bf(wl.make_conv_weight(cfg))
+    hidden = bf(wl.make_hidden(cfg, T=T))
+    toks, qsl, acc = it(toks_h), it(qsl_h), it(acc_h)
+    hashes = [ple.HashParams(b.multipliers[l], b.vocab_sizes, b.offsets, heads_per_ngram=cfg.heads_per_ngram,
+                             context_len=cfg.context_len, eos_token_id=wl.EOS) for l in range(L)]
+    layers = [ple.Layer(hashes[l], tb, kv_ws[l % 4], conv_w, conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+              for l in range(L)]
+    nbytes = ple.ple_prefill_workspace_bytes(layers[0], T)
+    ws = [torch.empty((nbytes,), dtype=torch.uint8, device=dev) for _ in range(L)]
+    xs = [ple.prefill_conv_input(layers[l], ws[l], T) for l in range(L)]
+    # per layer: the state and context the step starts from, and the committed ones
+    st = [[bf(b.conv_state), torch.empty((R, cfg.S, cfg.N), dtype=torch.bfloat16, device=dev)] for _ in range(L)]
+    ctx = [[it(b.ngram_context), torch.empty((R, cfg.context_len), dtype=torch.int32, device=dev)]
+           for _ in range(L)]
+    out = torch.empty((T, cfg.N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def verify(s):
+        l = s % L
+        ple.ple_prefill_fused(layers[l], toks, qsl, hidden, ngram_context=ctx[l][0], conv_state=st[l][0], out=out,
+                              workspace=ws[l])
+
+    def commit(s):
+        l = s % L
+        ple.ple_spec_commit(toks, qsl, acc, hash=hashes[l], ngram_context=ctx[l][0], ngram_context_out=ctx[l][1],
+                            x=xs[l], conv_kernel=cfg.conv_kernel, conv_dilation=cfg.conv_dilation,
+                            conv_state=st[l][0], conv_state_out=st[l][1])
+
+    def step(s):
+        verify(s)
+        commit(s)
+        l = s % L
+        st[l].reverse()
+        ctx[l].reverse()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for s in range(max(args.warmup, L)):
+        step(s)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    # The same step as a HIP graph per layer (verify + commit; the library
+    # allocates nothing and clears nothing with memset, so the calls capture
+    # as plain kernel nodes), replayed the way a serving loop would.
+    graphs = []
+    for l in range(L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            verify(l)
+            commit(l)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        graphs[s % L].replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+
+    def graph_of(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        return g
+
+    reps = 4 * L
+    g_verify, g_commit = graph_of(verify, reps), graph_of(commit, reps)
+    verify_ms = min(timed(lambda i: g_verify.replay(), 4) for _ in range(3)) / reps
+    commit_ms = min(timed(lambda i: g_commit.replay(), 4) for _ in range(3)) / reps
+    S, N, C = cfg.S, cfg.N, cfg.context_len
+    # each committed state row is read once (from the old state or the window) and written once
+    commit_bytes = 2 * R * S * N * 2 + 2 * R * C * 4 + R * 4 + (R + 1) * 4
+    line = {"metric": "tokens/s, speculative verify + state commit, decode-shaped model (one layer)",
+            "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "spec-decode-256x4", "requests": R, "window": W, "tokens": T,
+                       "accepted_mean": round(float(acc_h.mean()), 3), "heads": cfg.H, "table_rows": cfg.num_rows,
+                       "dim": cfg.D, "hidden": N, "conv": [cfg.conv_kernel, cfg.conv_dilation],
+                       "context_len": C, "layers_rotated": L},
+            "committed_tokens_per_s": round(float(acc_h.sum()) / (ms_per_step * 1e-3), 1),
+            "step_timing": "HIP graph per layer step, replayed",
+            "eager_ms_per_step": round(eager_ms, 4),
+            "verify_ms": round(verify_ms, 5),
+            "commit": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
+                       "GBps": round(commit_bytes / (commit_ms * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(commit_bytes / (commit_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
     print(json.dumps(line), flush=True)
     return 0
 

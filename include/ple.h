@@ -11,6 +11,7 @@
  *   ple_gate       sigmoid gate of the RMS-normalised hidden.key product, times value
  *   ple_conv       dilated causal depthwise short convolution
  *   ple_prefill_fused  all of the above in stream order
+ *   ple_spec_commit    conv state and n-gram context after speculative verify
  *
  * Sources (page title, then section):
  *   [P1] "PR #54371 [Qwen4Exp] Support UVA PLE-offload and Engram tensor
@@ -243,6 +244,11 @@ int ple_conv(const uint16_t* x, const ple_batch_desc* batch, const uint16_t* w, 
  * or NULL; workspace: device memory of at least
  * ple_prefill_workspace_bytes(layer, T) bytes, 256-byte aligned (holds rows,
  * kv and the gated value between kernels; not read before being written).
+ * On return the conv input (the gated value, bf16 [T][N]) stays in the
+ * workspace at byte offset round256(T*H*D*2) + round256(T*2N*2), where
+ * round256 rounds up to a multiple of 256 and T = batch->num_tokens: a
+ * speculative verify step that keeps one workspace per layer passes that
+ * region as x to ple_spec_commit.
  */
 int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
                       const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* workspace,
@@ -306,6 +312,28 @@ int ple_head_shard(int32_t num_heads, int32_t tp_size, int32_t tp_rank, int32_t 
  */
 int ple_select_rows(const uint16_t* gathered, int32_t num_shards, int64_t slot, int32_t rank, int64_t num_tokens,
                     int32_t width, uint16_t* out, void* stream);
+
+/*
+ * Speculative decode commit ([P3] 实现拆解 items 4-5: the conv's speculative
+ * variant and the state the short-conv backend carries between steps).  A
+ * verify step runs ple_ngram_ids / ple_conv over each request's whole
+ * candidate window [a, b) = [qsl[r], qsl[r+1]) (token 0 is the last accepted
+ * token, the rest are drafts); afterwards only the first accepted[r] of them
+ * are kept.  This call writes the state the next step starts from as if only
+ * those had been run, so rejected drafts leave no trace:
+ *   conv_state_out[r]    = last S rows of conv_state[r] ++ x[a : a+acc_r]
+ *   ngram_context_out[r] = last C tokens of ngram_context[r] ++
+ *                          input_ids[a : a+acc_r]
+ * with acc_r = accepted[r] clamped to 0..b-a (conv_state / ngram_context NULL
+ * read as zeros / EOS, as in ple_conv and ple_ngram_ids).  accepted: device
+ * int32 [R], read on the device, so out-of-range counts are clamped rather than
+ * reported.  x: the conv input of the verify step, device bf16 [T][N] (may be
+ * NULL when batch->conv_state_out is NULL).  hash supplies C and EOS (may be
+ * NULL when batch->ngram_context_out is NULL).  Either output may be NULL; the
+ * input states are only read.  S = (conv_kernel - 1) * conv_dilation.
+ */
+int ple_spec_commit(const ple_hash_desc* hash, const ple_batch_desc* batch, const int32_t* accepted,
+                    const uint16_t* x, int32_t n, int32_t conv_kernel, int32_t conv_dilation, void* stream);
 
 /* Message for the last failure on the calling thread ("" if none). */
 const char* ple_error_message(void);

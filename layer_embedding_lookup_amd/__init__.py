@@ -29,7 +29,8 @@ from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_DTYPE_FP8_E4M3_GLOBAL
 __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_lookup", "ple_prefetch",
            "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes", "ple_dp_gather_slot", "ple_head_shard",
            "ple_select_rows",
-           "ple_kv_proj", "ple_gate", "ple_conv", "ple_prefill_fused", "ple_prefill_workspace_bytes",
+           "ple_kv_proj", "ple_gate", "ple_conv", "ple_spec_commit", "ple_prefill_fused", "ple_prefill_workspace_bytes",
+           "prefill_conv_input",
            "ple_host_alloc", "ple_host_free", "HostBuffer", "ple_stream_create_cu_masked", "ple_stream_destroy",
            "ple_error_message", "ple_version", "library"]
 
@@ -267,9 +268,31 @@ def ple_conv(x, query_start_loc, w, *, dilation: int, conv_state=None, conv_stat
     return y
 
 
+def ple_spec_commit(input_ids, query_start_loc, accepted, *, hash: HashParams = None, ngram_context=None,
+                    ngram_context_out=None, x=None, conv_kernel: int = 1, conv_dilation: int = 1, conv_state=None,
+                    conv_state_out=None, stream=None):
+    """State after a speculative verify step that keeps accepted[r] tokens of request r."""
+    N = int(x.shape[1]) if x is not None else (int(conv_state_out.shape[2]) if conv_state_out is not None else 0)
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out,
+               num_tokens=None if input_ids is not None else (x.shape[0] if x is not None else 0))
+    h = hash.desc() if hash is not None else None
+    capi.check(capi.load().ple_spec_commit(ctypes.byref(h) if h is not None else None, ctypes.byref(b),
+                                           _ptr(accepted), _ptr(x), N, conv_kernel, conv_dilation, _stream(stream)),
+               "ple_spec_commit")
+
+
 def ple_prefill_workspace_bytes(layer: Layer, max_tokens: int) -> int:
     L = layer.desc()
     return int(capi.load().ple_prefill_workspace_bytes(ctypes.byref(L), int(max_tokens)))
+
+
+def prefill_conv_input(layer: Layer, workspace, num_tokens: int):
+    """View of the conv input (gated value, bf16 [T][N]) a ple_prefill_fused call leaves in its workspace."""
+    def r256(n):
+        return (n + 255) // 256 * 256
+    T, N = int(num_tokens), layer.hidden
+    off = r256(T * layer.hash.num_heads * layer.table.dim * 2) + r256(T * 2 * N * 2)
+    return workspace[off:off + T * N * 2].view(torch.bfloat16).view(T, N)
 
 
 def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefetched_rows=None, ngram_context=None,

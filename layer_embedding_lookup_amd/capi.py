@@ -69,6 +69,8 @@ _PROTOS = {
     "ple_kv_proj": (ctypes.c_int, [P, P, I64, I32, I32, P, P]),
     "ple_gate": (ctypes.c_int, [P, P, I64, I32, ctypes.c_float, P, P, P]),
     "ple_conv": (ctypes.c_int, [P, ctypes.POINTER(ple_batch_desc), P, I32, I32, I32, P, P]),
+    "ple_spec_commit": (ctypes.c_int, [ctypes.POINTER(ple_hash_desc), ctypes.POINTER(ple_batch_desc), P, P, I32,
+                                       I32, I32, P]),
     "ple_prefill_fused": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P, P, P,
                                          P, P, ctypes.c_size_t, P]),
     "ple_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ple_layer_desc), I64]),

@@ -543,6 +543,48 @@ int ple_conv(const uint16_t* x, const ple_batch_desc* batch, const uint16_t* w, 
     return rc ? rc : ok();
 }
 
+int ple_spec_commit(const ple_hash_desc* hash, const ple_batch_desc* batch, const int32_t* accepted,
+                    const uint16_t* x, int32_t n, int32_t conv_kernel, int32_t conv_dilation, void* stream) {
+    if (batch == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "batch descriptor is NULL");
+    const bool ctx_work = batch->ngram_context_out != nullptr;
+    const bool conv_work = batch->conv_state_out != nullptr;
+    int rc = validate_batch_conv(batch);
+    if (rc) return rc;
+    if (ctx_work) {
+        HashParams hp;
+        rc = validate_hash(hash, &hp);
+        if (rc) return rc;
+        rc = validate_batch_tokens(batch);
+        if (rc) return rc;
+    }
+    int S = 0;
+    if (conv_work) {
+        if (n < 8 || n % 8 != 0) return fail(PLE_ERR_UNSUPPORTED, "hidden size %d is not a positive multiple of 8", n);
+        if (conv_kernel < 1 || conv_kernel > 16)
+            return fail(PLE_ERR_INVALID_ARGUMENT, "conv kernel %d outside 1..16", conv_kernel);
+        if (conv_dilation < 1) return fail(PLE_ERR_INVALID_ARGUMENT, "conv dilation %d < 1", conv_dilation);
+        if ((int64_t)(conv_kernel - 1) * conv_dilation > 4096)
+            return fail(PLE_ERR_INVALID_ARGUMENT, "conv span (K-1)*d exceeds 4096");
+        S = (conv_kernel - 1) * conv_dilation;
+        if (batch->num_tokens > 0 && (x == nullptr || !aligned16(x)))
+            return fail(PLE_ERR_INVALID_ARGUMENT, "conv input x is NULL or not 16-byte aligned");
+    }
+    if (batch->num_reqs > 0 && (accepted == nullptr || !aligned4(accepted)))
+        return fail(PLE_ERR_INVALID_ARGUMENT, "accepted is NULL or misaligned");
+    const bool do_ctx = ctx_work && batch->num_reqs > 0 && hash->context_len > 0;
+    const bool do_conv = conv_work && batch->num_reqs > 0 && S > 0;
+    if (!do_ctx && !do_conv) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    hipError_t e = launch_spec_commit(batch->input_ids, x, batch->query_start_loc, batch->num_tokens,
+                                      batch->num_reqs, accepted, batch->conv_state, n, S,
+                                      do_conv ? batch->conv_state_out : nullptr, batch->ngram_context,
+                                      do_ctx ? hash->context_len : 0, do_ctx ? hash->eos_token_id : 0,
+                                      do_ctx ? batch->ngram_context_out : nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "spec commit launch");
+    return ok();
+}
+
 size_t ple_prefill_workspace_bytes(const ple_layer_desc* layer, int64_t max_tokens) {
     if (layer == nullptr || max_tokens <= 0) return 0;
     const size_t T = (size_t)max_tokens;

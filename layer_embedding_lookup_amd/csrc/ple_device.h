@@ -134,4 +134,55 @@ __device__ __forceinline__ void wave_find_request(const int32_t* __restrict__ qs
     a_out = a < 0 ? 0 : (a > t ? t : a);  // keeps every read in bounds for any qsl
 }
 
+// Tokens of request r that the carried state and context take in: [a, b) =
+// [qsl[r], qsl[r+1]) clamped to [0, T]; with accepted (speculative decode) only
+// the first accepted[r] of them.
+__device__ __forceinline__ void carried_window(const int32_t* __restrict__ qsl, int64_t T, int r,
+                                               const int32_t* __restrict__ accepted, int64_t& a, int64_t& b) {
+    a = qsl[r];
+    b = qsl[r + 1];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    b = b < a ? a : (b > T ? T : b);
+    if (accepted != nullptr) {
+        const int64_t acc = accepted[r];
+        b = acc <= 0 ? a : (a + acc < b ? a + acc : b);
+    }
+}
+
+// One wave writes carried conv state row m of request r: row (b-a)+m of
+// state[r] ++ x[a:b] (state NULL reads as zeros), N bf16 in 16-byte chunks,
+// lane-contiguous, four chunks in flight per lane.
+__device__ __forceinline__ void carry_state_row(const uint16_t* __restrict__ x, const uint16_t* __restrict__ state,
+                                                int N, int S, int r, int m, int64_t a, int64_t b,
+                                                uint16_t* __restrict__ state_out, int lane) {
+    const int64_t q = (b - a) + m;
+    const uint16_t* src = q >= S ? x + (a + (q - S)) * N
+                                 : (state != nullptr ? state + ((int64_t)r * S + q) * N : nullptr);
+    uint16_t* dst = state_out + ((int64_t)r * S + m) * N;
+    const int nch = N >> 3;
+    for (int c0 = 0; c0 < nch; c0 += 4 * kWave) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ch = c0 + u * kWave + lane;
+            v[u] = u32x4{0u, 0u, 0u, 0u};
+            if (src != nullptr && ch < nch) v[u] = *(const u32x4*)(src + ch * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ch = c0 + u * kWave + lane;
+            if (ch < nch) *(u32x4*)(dst + ch * 8) = v[u];
+        }
+    }
+}
+
+// Carried context entry i of request r: the (C-i)-th most recent raw token
+// of ctx[r] ++ tok[a:b] (ctx NULL reads as EOS).
+__device__ __forceinline__ int32_t carried_token(const int32_t* __restrict__ tok, const int32_t* __restrict__ ctx,
+                                                 int C, int32_t eos, int r, int i, int64_t a, int64_t b) {
+    const int64_t q = (b - a) + i;
+    if (q >= C) return tok[a + (q - C)];
+    return ctx != nullptr ? ctx[(int64_t)r * C + q] : eos;
+}
+
 }  // namespace ple

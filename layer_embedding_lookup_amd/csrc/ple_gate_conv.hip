@@ -488,24 +488,16 @@ __global__ __launch_bounds__(256) void conv_state_out_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ qsl, int64_t T, int R,
                                                              const uint16_t* __restrict__ state, int N, int S,
                                                              uint16_t* __restrict__ state_out) {
-    const int nch = N >> 3;
-    const int64_t total = (int64_t)R * S * nch;
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
-         p += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t rm = p / nch;
-        const int ch = (int)(p - rm * nch);
-        const int r = (int)(rm / S);
-        const int m = (int)(rm - (int64_t)r * S);
-        int64_t a = qsl[r], b = qsl[r + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        b = b < a ? a : (b > T ? T : b);
-        const int64_t q = (b - a) + m;  // index into state[r] ++ x[a:b]
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (q >= S)
-            v = *(const u32x4*)(x + (a + (q - S)) * N + ch * 8);
-        else if (state != nullptr)
-            v = *(const u32x4*)(state + ((int64_t)r * S + q) * N + ch * 8);
-        *(u32x4*)(state_out + ((int64_t)r * S + m) * N + ch * 8) = v;
+    // one wave per state row (r, m)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t rows = (int64_t)R * S;
+    const int wpb = blockDim.x / kWave;
+    for (int64_t w = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave; w < rows; w += (int64_t)gridDim.x * wpb) {
+        const int r = (int)(w / S);
+        const int m = (int)(w - (int64_t)r * S);
+        int64_t a, b;
+        carried_window(qsl, T, r, nullptr, a, b);
+        carry_state_row(x, state, N, S, r, m, a, b, state_out, lane);
     }
 }
 
@@ -549,9 +541,8 @@ hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, 
 
 hipError_t launch_conv_state_out(const uint16_t* x, const int32_t* qsl, int64_t T, int R,
                                  const uint16_t* state, int N, int S, uint16_t* state_out, hipStream_t s) {
-    const int64_t total = (int64_t)R * S * (N >> 3);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > (1 << 20)) blocks = 1 << 20;
+    int64_t blocks = ((int64_t)R * S + 3) / 4;
+    if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(conv_state_out_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, qsl, T, R, state, N, S,
                        state_out);
     return hipGetLastError();

@@ -54,18 +54,9 @@ __global__ __launch_bounds__(256) void context_out_kernel(const int32_t* __restr
          p += (int64_t)gridDim.x * blockDim.x) {
         const int r = (int)(p / C);
         const int i = (int)(p - (int64_t)r * C);
-        int64_t a = qsl[r], b = qsl[r + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        b = b < a ? a : (b > T ? T : b);
-        const int64_t q = (b - a) + i;  // index into ctx[r] ++ tok[a:b]
-        int32_t v;
-        if (q >= C)
-            v = tok[a + (q - C)];
-        else if (ctx != nullptr)
-            v = ctx[(int64_t)r * C + q];
-        else
-            v = eos;
-        ctx_out[p] = v;
+        int64_t a, b;
+        carried_window(qsl, T, r, nullptr, a, b);
+        ctx_out[p] = carried_token(tok, ctx, C, eos, r, i, a, b);
     }
 }
 

@@ -227,6 +227,43 @@ def conv(x, qsl, w, dilation, state=None, want_state_out=False):
     return (y, so) if want_state_out else y
 
 
+def spec_commit(input_ids, x, qsl, accepted, *, conv_kernel, dilation, conv_state=None, hash_args=None,
+                ngram_context=None):
+    """Carried state after a speculative verify step ("Fuse Qwen4Exp PLE kernels",
+    实现拆解 items 4-5: the conv's speculative variant and the short-conv state).
+
+    Request r's window is [qsl[r], qsl[r+1]); only its first accepted[r] tokens
+    (clamped to 0..window length) are kept.  By definition the committed state
+    is the state the plain path leaves when run on the batch that holds only the
+    kept tokens, so this builds that batch and calls ``conv`` and
+    ``ngram_ids`` on it.  Returns (conv_state_out [R, S, N] or None,
+    ngram_context_out [R, C] or None); x is None skips the conv part and
+    hash_args (the keyword arguments of ``ngram_ids`` other than the batch) None
+    skips the context part.
+    """
+    q = np.asarray(qsl, dtype=np.int64)
+    R = q.shape[0] - 1
+    keep = []
+    new_q = [0]
+    for r in range(R):
+        a, b = int(q[r]), int(q[r + 1])
+        acc = min(max(int(accepted[r]), 0), b - a)
+        keep.extend(range(a, a + acc))
+        new_q.append(new_q[-1] + acc)
+    keep = np.asarray(keep, dtype=np.int64)
+    new_q = np.asarray(new_q, dtype=np.int32)
+    state_out = ctx_out = None
+    if x is not None:
+        x = np.asarray(x, dtype=np.uint16)
+        N = x.shape[1]
+        w = np.zeros((N, conv_kernel), dtype=np.uint16)
+        _, state_out = conv(x[keep].reshape(-1, N), new_q, w, dilation, state=conv_state, want_state_out=True)
+    if hash_args is not None:
+        tok = np.asarray(input_ids, dtype=np.int32)[keep]
+        _, ctx_out = ngram_ids(tok, new_q, ngram_context=ngram_context, want_context_out=True, **hash_args)
+    return state_out, ctx_out
+
+
 def prefill(batch_ids_args: dict, table, scales, hidden, kv_weight, conv_weight, dilation, *,
             qsl, eps=1e-6, conv_state=None, tokens=None):
     """Whole path: ids -> rows -> kv -> gate -> conv.

@@ -21,7 +21,7 @@ FAKE = 1 << 40  # a 256-aligned address that is never dereferenced: every call b
 
 def test_exports_every_header_function():
     names = capi.header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(capi._PROTOS)
@@ -190,3 +190,27 @@ def test_dedup_workspace_size_and_limits():
     big = capi.ple_batch_desc(FAKE, FAKE, 1 << 21, 2, 0, None, None, None, None)
     assert lib.ple_prefetch_dedup(ctypes.byref(layer), ctypes.byref(big), FAKE, FAKE, 1 << 30, None, None) == E_UNSUP
     assert lib.ple_prefetch_dedup(None, ctypes.byref(b), FAKE, FAKE, 1 << 20, None, None) == E_ARG
+
+
+def test_spec_commit_rejects_and_noops():
+    h, keep = _hash()
+    acc = FAKE + 512
+    # Nothing to write: returns before any device call.
+    assert lib.ple_spec_commit(ctypes.byref(h), ctypes.byref(_batch()), acc, FAKE, 16, 4, 1, None) == capi.PLE_OK
+    assert lib.ple_spec_commit(ctypes.byref(h), ctypes.byref(_batch(T=0, R=0, ctx_out=FAKE, state_out=FAKE)), None,
+                               None, 16, 4, 1, None) == capi.PLE_OK
+    assert lib.ple_spec_commit(ctypes.byref(h), None, acc, FAKE, 16, 4, 1, None) == E_ARG
+    # Context output needs the hash (C, EOS); conv state output needs a valid conv shape and x.
+    assert lib.ple_spec_commit(None, ctypes.byref(_batch(ctx_out=FAKE)), acc, None, 0, 1, 1, None) == E_ARG
+    bs = _batch(state_out=FAKE)
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), acc, FAKE, 12, 4, 1, None) == E_UNSUP
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), acc, FAKE, 16, 17, 1, None) == E_ARG
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), acc, FAKE, 16, 4, 0, None) == E_ARG
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), acc, None, 16, 4, 1, None) == E_ARG
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), acc, FAKE + 2, 16, 4, 1, None) == E_ARG
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), None, FAKE, 16, 4, 1, None) == E_ARG
+    assert "accepted" in _msg()
+    assert lib.ple_spec_commit(None, ctypes.byref(bs), acc + 2, FAKE, 16, 4, 1, None) == E_ARG
+    b_alias = _batch(state=FAKE + 256, state_out=FAKE + 256)
+    assert lib.ple_spec_commit(None, ctypes.byref(b_alias), acc, FAKE, 16, 4, 1, None) == E_ARG
+    assert "alias" in _msg()

@@ -657,3 +657,170 @@ def test_sharded_lookup_equals_unsharded():
         full = ple.ple_lookup(hash_params(b), tb, dev(b.input_ids[s0:s0 + counts[r]]), dev(qr),
                               ngram_context=dev(b.ngram_context[s0:s0 + counts[r]]))
         assert torch.equal(mine.view(torch.int16), full.view(torch.int16)), r
+
+
+# ------------------------------------------------------------------ speculative decode commit
+
+def _spec_hash(C, seed):
+    H = 2 * C
+    V = wl.primes_from(1000 + 50 * seed, H)
+    off = np.concatenate([[0], np.cumsum(V)[:-1]]).astype(np.int64)
+    m = wl.multipliers(seed, 1, H, C + 1)[0]
+    return dict(multipliers=m, vocab_sizes=np.asarray(V, np.int64), offsets=off, context_len=C,
+                heads_per_ngram=2, eos_token_id=wl.EOS)
+
+
+SPEC_CASES = [
+    # (R, max_window, N, K, d, C, with_state)
+    (256, 4, 2048, 4, 3, 2, True),    # decode-shaped batch, 3 drafts per request
+    (256, 4, 2048, 4, 3, 2, False),
+    (37, 9, 64, 7, 2, 3, True),       # wider windows than the state, generic kernel size
+    (5, 1, 8, 2, 1, 1, True),         # one-token windows: plain decode
+    (6, 0, 16, 4, 3, 2, True),        # empty windows: state passes through
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPEC_CASES)))
+def test_spec_commit_parity(case):
+    R, maxw, N, K, d, C, with_state = SPEC_CASES[case]
+    log(f"spec commit case {case}: R={R} window<={maxw} N={N} K={K} d={d} C={C} state={with_state}")
+    S = (K - 1) * d
+    lens = wl.uniform_ints(900 + case, R, 0 if maxw == 0 else 1, maxw + 1) if maxw else np.zeros(R, np.int64)
+    qsl = wl.qsl_from_lengths(lens)
+    T = int(qsl[-1])
+    tok = wl.uniform_ints(910 + case, T, 1, 151936).astype(np.int32)
+    x = wl.normal_bf16((T, N), 920 + case, 0.5)
+    # Counts cover -1 .. window+1 so both clamps are exercised.
+    acc = (wl.uniform_ints(930 + case, R, 0, 1 << 20) % (lens + 3) - 1).astype(np.int32)
+    st = wl.normal_bf16((R, S, N), 940 + case, 0.25) if with_state else None
+    ctx = wl.uniform_ints(950 + case, R * C, 1, 151936).astype(np.int32).reshape(R, C) if with_state else None
+    ha = _spec_hash(C, case)
+    st_want, ctx_want = oracle.spec_commit(tok, x, qsl, acc, conv_kernel=K, dilation=d, conv_state=st,
+                                           hash_args=ha, ngram_context=ctx)
+    hp = ple.HashParams(ha["multipliers"], ha["vocab_sizes"], ha["offsets"], heads_per_ngram=2, context_len=C,
+                        eos_token_id=wl.EOS)
+    st_out = torch.full((R, S, N), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ctx_out = torch.full((R, C), -7, dtype=torch.int32, device=DEV)
+    xd = dev_bf16(x) if T else torch.zeros((0, N), dtype=torch.bfloat16, device=DEV)
+    ple.ple_spec_commit(dev(tok) if T else torch.zeros(0, dtype=torch.int32, device=DEV), dev(qsl), dev(acc),
+                        hash=hp, ngram_context=None if ctx is None else dev(ctx), ngram_context_out=ctx_out, x=xd,
+                        conv_kernel=K, conv_dilation=d, conv_state=None if st is None else dev_bf16(st),
+                        conv_state_out=st_out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(st_out), st_want)
+    np.testing.assert_array_equal(ctx_out.cpu().numpy(), ctx_want)
+
+
+def test_spec_decode_chain_matches_oracle():
+    """Three verify + commit steps: ids, conv output and carried state against the oracle's chain."""
+    R, N, K, d, C = 24, 64, 4, 3, 2
+    S = (K - 1) * d
+    ha = _spec_hash(C, 7)
+    hp = ple.HashParams(ha["multipliers"], ha["vocab_sizes"], ha["offsets"], heads_per_ngram=2, context_len=C,
+                        eos_token_id=wl.EOS)
+    w = wl.uniform_bf16((N, K), 960, -0.5, 0.5)
+    wd = dev_bf16(w)
+    st_o = np.zeros((R, S, N), np.uint16)
+    ctx_o = np.full((R, C), wl.EOS, np.int32)
+    st_g, ctx_g = dev_bf16(st_o), dev(ctx_o)
+    for step in range(3):
+        lens = wl.uniform_ints(970 + step, R, 1, 5)
+        qsl = wl.qsl_from_lengths(lens)
+        T = int(qsl[-1])
+        tok = wl.uniform_ints(980 + step, T, 1, 151936).astype(np.int32)
+        x = wl.normal_bf16((T, N), 990 + step, 0.5)
+        acc = (wl.uniform_ints(1000 + step, R, 0, 1 << 20) % lens + 1).astype(np.int32)
+        log(f"spec chain step {step}: T={T}")
+        ids_want = oracle.ngram_ids(tok, qsl, ngram_context=ctx_o, **ha)
+        y_want = oracle.conv(x, qsl, w, d, state=st_o)
+        st_o, ctx_o = oracle.spec_commit(tok, x, qsl, acc, conv_kernel=K, dilation=d, conv_state=st_o,
+                                         hash_args=ha, ngram_context=ctx_o)
+        tok_d, qsl_d, x_d = dev(tok), dev(qsl), dev_bf16(x)
+        ids = ple.ple_ngram_ids(hp, tok_d, qsl_d, ngram_context=ctx_g)
+        y = ple.ple_conv(x_d, qsl_d, wd, dilation=d, conv_state=st_g)
+        st_n = torch.empty((R, S, N), dtype=torch.bfloat16, device=DEV)
+        ctx_n = torch.empty((R, C), dtype=torch.int32, device=DEV)
+        ple.ple_spec_commit(tok_d, qsl_d, dev(acc), hash=hp, ngram_context=ctx_g, ngram_context_out=ctx_n, x=x_d,
+                            conv_kernel=K, conv_dilation=d, conv_state=st_g, conv_state_out=st_n)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_want)
+        got = host_bits(y)
+        assert np.abs(bf16_f64(got) - bf16_f64(y_want)).max() <= CONV_ABS_TOL
+        assert bf16_ulp_distance(got, y_want).max() <= 1
+        np.testing.assert_array_equal(host_bits(st_n), st_o)
+        np.testing.assert_array_equal(ctx_n.cpu().numpy(), ctx_o)
+        st_g, ctx_g = st_n, ctx_n
+
+
+def test_spec_verify_fused_then_commit():
+    """Verify window through ple_prefill_fused, then commit from the conv input left in its workspace."""
+    cfg = wl.CONFIGS[1]
+    b = wl.make_batch(cfg, with_context=True, with_state=True)
+    L, table, scales, kvw, cw, keep = _layer(cfg, b)
+    hidden = wl.make_hidden(cfg)
+    ref = _oracle_chain(cfg, b, table, scales, kvw, cw, hidden)
+    acc = np.asarray([3, 1, 0, 3], np.int32)   # windows are 7, 1, 13, 3 tokens
+    st_want, ctx_want = oracle.spec_commit(
+        b.input_ids, ref["gated"], b.qsl, acc, conv_kernel=cfg.conv_kernel, dilation=cfg.conv_dilation,
+        conv_state=b.conv_state, ngram_context=b.ngram_context,
+        hash_args=dict(multipliers=b.multipliers[0], vocab_sizes=b.vocab_sizes, offsets=b.offsets,
+                       context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS))
+    T = cfg.T
+    ws = torch.empty((ple.ple_prefill_workspace_bytes(L, T),), dtype=torch.uint8, device=DEV)
+    toks, qsl = dev(b.input_ids), dev(b.qsl)
+    ctx, st = dev(b.ngram_context), dev_bf16(b.conv_state)
+    out = ple.ple_prefill_fused(L, toks, qsl, dev_bf16(hidden), ngram_context=ctx, conv_state=st, workspace=ws)
+    assert np.abs(bf16_f64(host_bits(out)) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
+    x = ple.prefill_conv_input(L, ws, T)
+    assert np.abs(bf16_f64(host_bits(x)) - bf16_f64(ref["gated"])).max() <= GATE_ABS_TOL
+    st_out = torch.empty((b.R, cfg.S, cfg.N), dtype=torch.bfloat16, device=DEV)
+    ctx_out = torch.empty((b.R, cfg.context_len), dtype=torch.int32, device=DEV)
+    ple.ple_spec_commit(toks, qsl, dev(acc), hash=L.hash, ngram_context=ctx, ngram_context_out=ctx_out, x=x,
+                        conv_kernel=cfg.conv_kernel, conv_dilation=cfg.conv_dilation, conv_state=st,
+                        conv_state_out=st_out)
+    np.testing.assert_array_equal(ctx_out.cpu().numpy(), ctx_want)
+    assert np.abs(bf16_f64(host_bits(st_out)) - bf16_f64(st_want)).max() <= GATE_ABS_TOL
+    # request 2 kept nothing: its state is the input state, bit for bit
+    np.testing.assert_array_equal(host_bits(st_out)[2], b.conv_state[2])
+
+
+def test_spec_step_graph_replay_matches_eager():
+    """Verify + commit captured in a HIP graph: every replay equals the eager step, with eager work in between."""
+    cfg = wl.CONFIGS[2]
+    b = wl.make_batch(cfg)
+    L, *_ = _layer(cfg, b)
+    W, R = 2, 64
+    T = R * W
+    toks = dev(wl.make_tokens(cfg, T=T))
+    qsl = dev(np.arange(0, T + 1, W, dtype=np.int32))
+    acc = dev(wl.uniform_ints(1234, R, 0, W + 2))
+    hidden = dev_bf16(wl.make_hidden(cfg, T=T))
+    ctx, st = dev(b.ngram_context[:R]), dev_bf16(b.conv_state[:R])
+    ws = torch.empty((ple.ple_prefill_workspace_bytes(L, T),), dtype=torch.uint8, device=DEV)
+    x = ple.prefill_conv_input(L, ws, T)
+    out = torch.empty((T, cfg.N), dtype=torch.bfloat16, device=DEV)
+    st_out = torch.empty((R, cfg.S, cfg.N), dtype=torch.bfloat16, device=DEV)
+    ctx_out = torch.empty((R, cfg.context_len), dtype=torch.int32, device=DEV)
+
+    def step():
+        ple.ple_prefill_fused(L, toks, qsl, hidden, ngram_context=ctx, conv_state=st, out=out, workspace=ws)
+        ple.ple_spec_commit(toks, qsl, acc, hash=L.hash, ngram_context=ctx, ngram_context_out=ctx_out, x=x,
+                            conv_kernel=cfg.conv_kernel, conv_dilation=cfg.conv_dilation, conv_state=st,
+                            conv_state_out=st_out)
+
+    step()
+    torch.cuda.synchronize()
+    want = [out.clone(), st_out.clone(), ctx_out.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (out, st_out, ctx_out):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"graph replay {rep}")
+        for got, w in zip((out, st_out, ctx_out), want):
+            assert torch.equal(got, w)
+        step()  # eager work between replays
+        torch.cuda.synchronize()
