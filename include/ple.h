@@ -207,8 +207,8 @@ size_t ple_prefetch_dedup_workspace_bytes(int64_t max_tokens, int32_t num_heads)
  * Merged key/value projection ([P3] 实现拆解 item 1):
  *   kv[t][o] = bf16(sum_i x[t][i] * w[o][i]), fp32 accumulation, no bias.
  * x: device bf16 [T][K]; w: device bf16 [O][K]; kv: device bf16 [T][O].
- * K a multiple of 64, O a multiple of 16, T <= PLE_MAX_TOKENS and
- * ceil(T/128) * ceil(O/128) <= 2^24 (else PLE_ERR_UNSUPPORTED).
+ * K a multiple of 64 and at most 2^20, O a multiple of 16, T <= PLE_MAX_TOKENS
+ * and ceil(T/128) * ceil(O/128) <= 2^24 (else PLE_ERR_UNSUPPORTED).
  */
 int ple_kv_proj(const uint16_t* x, const uint16_t* w, int64_t num_tokens, int32_t k_dim, int32_t out_dim,
                 uint16_t* kv, void* stream);

@@ -198,6 +198,7 @@ int validate_conv_shape(const uint16_t* w, int N, int K, int d) {
 int validate_gemm_shape(int K, int O) {
     if (K < 64 || K % 64 != 0) return fail(PLE_ERR_UNSUPPORTED, "kv_proj input width %d is not a multiple of 64", K);
     if (O < 16 || O % 16 != 0) return fail(PLE_ERR_UNSUPPORTED, "kv_proj output width %d is not a multiple of 16", O);
+    if (K > (1 << 20)) return fail(PLE_ERR_UNSUPPORTED, "kv_proj input width %d exceeds 2^20", K);
     return PLE_OK;
 }
 

@@ -103,6 +103,7 @@ def test_table_rejects():
 def test_kv_proj_gate_conv_reject():
     assert lib.ple_kv_proj(FAKE, FAKE, 10, 100, 256, FAKE, None) == E_UNSUP
     assert lib.ple_kv_proj(FAKE, FAKE, 10, 128, 250, FAKE, None) == E_UNSUP
+    assert lib.ple_kv_proj(FAKE, FAKE, 10, (1 << 20) + 64, 256, FAKE, None) == E_UNSUP
     assert lib.ple_kv_proj(None, FAKE, 10, 128, 256, FAKE, None) == E_ARG
     assert lib.ple_kv_proj(FAKE + 2, FAKE, 10, 128, 256, FAKE, None) == E_ARG
     assert lib.ple_kv_proj(FAKE, FAKE, -1, 128, 256, FAKE, None) == E_ARG
