@@ -249,7 +249,7 @@ LookupArgs lookup_args(const ple_table_desc* t, int H, int cpr_log2, const ple_b
     g.num_rows = t->num_rows;
     g.num_heads = H;
     g.dim = t->dim;
-    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dim / 8, t->dtype);
+    g.tokens_per_wave = lookup_tokens_per_wave(H, t->dim / 8, t->dtype, T);
     g.cpr_log2 = cpr_log2;
     return g;
 }

@@ -35,7 +35,7 @@ hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int3
                             const int32_t* ctx, int32_t* ids, hipStream_t s);
 hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T, int R, int C, int32_t eos,
                               const int32_t* ctx, int32_t* ctx_out, hipStream_t s);
-int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype);
+int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype, int64_t num_tokens);
 hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s);
 
 hipError_t launch_dedup(const int32_t* ids, int64_t n, int32_t* keys, int32_t* rep, int log2cap,

@@ -286,12 +286,16 @@ static int lookup_loads(int dtype) {
     return dtype == PLE_DTYPE_BF16 ? PLE_LOOKUP_LOADS : (dtype == PLE_DTYPE_NVFP4 ? PLE_LOOKUP_LOADS_FP4 : PLE_LOOKUP_LOADS_FP8);
 }
 
-int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype) {
+int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype, int64_t num_tokens) {
     // about lookup_loads(dtype) output chunks per lane, at most 64 rows (one
     // lane per row for the IDs); chunks_per_row counts 16-byte output chunks
     const int chunks_per_token = H * chunks_per_row;
     int tw = (lookup_loads(dtype) * kWave) / chunks_per_token;
     if (tw > kWave / H) tw = kWave / H;
+    // small batches (decode, speculative verify): fewer tokens per wave so
+    // that the grid still gives every SIMD of the 256 CUs a wave
+    const int64_t fill = (num_tokens + 1023) / 1024;
+    if (tw > fill) tw = (int)fill;
     return tw < 1 ? 1 : tw;
 }
 
