@@ -47,9 +47,10 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill-8k-bf16-hbm",
                     choices=["prefill-8k-bf16-hbm", "prefill-16k-fp8-hbm", "prefill-16k-fp8global-hbm",
                              "prefill-8k-nvfp4-hbm", "prefill-8k-bf16-host", "select-rows-8k",
-                             "spec-decode-256x4"],
+                             "spec-decode-256x4", "decode-256"],
                     help="the default is the benchmark line; the others report the fp8-table (per-row or "
-                         "one global scale), NVFP4-table and host-resident-table variants")
+                         "one global scale), NVFP4-table and host-resident-table variants, the row select of a "
+                         "sharded table, and the decode and speculative-decode steps of the decode-shaped model")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -70,6 +71,8 @@ def main() -> int:
         return bench_select_rows(args)
     if args.workload == "spec-decode-256x4":
         return bench_spec_decode(args)
+    if args.workload == "decode-256":
+        return bench_decode(args)
     # table format of the workload; the batch, projection and conv are those of
     # the 8k prefill (bf16, NVFP4) or the 16k prefill (fp8 tables)
     fmt = {"prefill-8k-bf16-hbm": "bf16", "prefill-16k-fp8-hbm": "fp8", "prefill-16k-fp8global-hbm": "fp8-global",
@@ -450,14 +453,109 @@ def bench_select_rows(args):
     return 0
 
 
+def bench_decode(args):
+    """Decode on the decode-shaped model: 256 requests of one new token each
+    with a 2-token n-gram context and a 9-row conv state, 8 heads over a
+    ~1M x 256 bf16 table, hidden 2048, kv_proj 2048 -> 2x2048, conv 4 /
+    dilation 3.  A step is one layer's fused path that also writes the next
+    context and conv state, timed eagerly; the same step replayed as a HIP
+    graph per layer is reported beside it."""
+    import numpy as np
+    import torch
+
+    import layer_embedding_lookup_amd as ple
+    import workloads as wl
+
+    dev = "cuda:0"
+    cfg = wl.CONFIGS[2]
+    L = args.layers
+    T = R = cfg.T
+    b = wl.make_batch(cfg, layers=L)
+    log(f"decode: R={R} T={T} rows={cfg.num_rows} D={cfg.D} N={cfg.N}")
+    table_h, _ = wl.make_table(cfg)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def it(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    tb = ple.Table.from_tensor(bf(table_h))
+    kv_ws = [bf(wl.make_kv_weight(cfg, layer=i)) for i in range(4)]
+    conv_w = bf(wl.make_conv_weight(cfg))
+    hidden = bf(wl.make_hidden(cfg))
+    toks, qsl = it(b.input_ids), it(b.qsl)
+    hashes = [ple.HashParams(b.multipliers[l], b.vocab_sizes, b.offsets, heads_per_ngram=cfg.heads_per_ngram,
+                             context_len=cfg.context_len, eos_token_id=wl.EOS) for l in range(L)]
+    layers = [ple.Layer(hashes[l], tb, kv_ws[l % 4], conv_w, conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+              for l in range(L)]
+    ws = torch.empty((ple.ple_prefill_workspace_bytes(layers[0], T),), dtype=torch.uint8, device=dev)
+    st = [[bf(b.conv_state), torch.empty((R, cfg.S, cfg.N), dtype=torch.bfloat16, device=dev)] for _ in range(L)]
+    ctx = [[it(b.ngram_context), torch.empty((R, cfg.context_len), dtype=torch.int32, device=dev)]
+           for _ in range(L)]
+    out = torch.empty((T, cfg.N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s, swap=True):
+        l = s % L
+        ple.ple_prefill_fused(layers[l], toks, qsl, hidden, ngram_context=ctx[l][0], ngram_context_out=ctx[l][1],
+                              conv_state=st[l][0], conv_state_out=st[l][1], out=out, workspace=ws)
+        if swap:
+            st[l].reverse()
+            ctx[l].reverse()
+
+    for s in range(max(args.warmup, L)):
+        step(s)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    graphs = []
+    for l in range(L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(l, swap=False)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        graphs[s % L].replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    H, D, N, S = cfg.H, cfg.D, cfg.N, cfg.S
+    # HBM bytes of one step at one pass per array: table rows, rows out and
+    # back in, kv weight, kv out and back in, hidden, gated out and back in,
+    # output, conv state in and out, tokens, contexts
+    step_bytes = (3 * T * H * D * 2 + 2 * N * H * D * 2 + 2 * T * 2 * N * 2 + T * N * 2 + 2 * T * N * 2 + T * N * 2
+                  + 2 * R * S * N * 2 + T * 4 + 2 * R * cfg.context_len * 4)
+    line = {"metric": "tokens/s, decode step (one new token per request), decode-shaped model (one layer)",
+            "value": round(T / (eager_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(eager_ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "decode-256", "requests": R, "tokens": T, "heads": H, "table_rows": cfg.num_rows,
+                       "dim": D, "hidden": N, "kv_proj": [H * D, 2 * N], "conv": [cfg.conv_kernel, cfg.conv_dilation],
+                       "context_len": cfg.context_len, "layers_rotated": L},
+            "graph_ms_per_step": round(ms_per_step, 4),
+            "step_bytes": step_bytes,
+            "step_GBps": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_spec_decode(args):
     """Speculative decode on the decode-shaped model (256 requests, 8 heads over
     a ~1M x 256 bf16 table, hidden 2048, conv 4 / dilation 3): each request
     verifies a 4-token window (its last token and 3 drafts) through the fused
     path, then the carried conv state and n-gram context are committed for the
     1..4 accepted tokens (uniform).  A step is one layer's verify + commit,
-    timed as a replayed HIP graph (the eager loop's time is reported beside
-    it); verify and commit are each timed as graphs of back-to-back calls."""
+    timed eagerly (the same step replayed as a HIP graph per layer is reported
+    beside it); verify and commit are each timed as graphs of back-to-back
+    calls."""
     import numpy as np
     import torch
 
@@ -573,16 +671,15 @@ def bench_spec_decode(args):
     # each committed state row is read once (from the old state or the window) and written once
     commit_bytes = 2 * R * S * N * 2 + 2 * R * C * 4 + R * 4 + (R + 1) * 4
     line = {"metric": "tokens/s, speculative verify + state commit, decode-shaped model (one layer)",
-            "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "value": round(T / (eager_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(eager_ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "spec-decode-256x4", "requests": R, "window": W, "tokens": T,
                        "accepted_mean": round(float(acc_h.mean()), 3), "heads": cfg.H, "table_rows": cfg.num_rows,
                        "dim": cfg.D, "hidden": N, "conv": [cfg.conv_kernel, cfg.conv_dilation],
                        "context_len": C, "layers_rotated": L},
-            "committed_tokens_per_s": round(float(acc_h.sum()) / (ms_per_step * 1e-3), 1),
-            "step_timing": "HIP graph per layer step, replayed",
-            "eager_ms_per_step": round(eager_ms, 4),
+            "committed_tokens_per_s": round(float(acc_h.sum()) / (eager_ms * 1e-3), 1),
+            "graph_ms_per_step": round(ms_per_step, 4),
             "verify_ms": round(verify_ms, 5),
             "commit": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
                        "GBps": round(commit_bytes / (commit_ms * 1e-3) / 1e9, 1),
