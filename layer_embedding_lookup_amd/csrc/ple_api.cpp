@@ -654,12 +654,22 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
         e = launch_gate(hidden, kv, T, N, layer->eps, gated, gate, s);
         if (e != hipSuccess) return hip_fail(e, "gate launch");
     }
-    if (ctx_work) {
-        rc = run_context_out(&layer->hash, batch, s);
-        if (rc) return rc;
+    if (T > 0) {
+        e = launch_conv(gated, batch->query_start_loc, T, batch->num_reqs, batch->conv_state, layer->conv_weight, N,
+                        layer->conv_kernel, layer->conv_dilation, out, s);
+        if (e != hipSuccess) return hip_fail(e, "conv launch");
     }
-    rc = run_conv(gated, batch, layer->conv_weight, N, layer->conv_kernel, layer->conv_dilation, out, s);
-    return rc ? rc : ok();
+    // the carried context and conv state in one launch (the commit kernel
+    // over every request's whole window)
+    if (ctx_work || state_work) {
+        const int S = (layer->conv_kernel - 1) * layer->conv_dilation;
+        e = launch_spec_commit(batch->input_ids, gated, batch->query_start_loc, T, batch->num_reqs, nullptr,
+                               batch->conv_state, N, S, state_work ? batch->conv_state_out : nullptr,
+                               batch->ngram_context, ctx_work ? layer->hash.context_len : 0,
+                               layer->hash.eos_token_id, ctx_work ? batch->ngram_context_out : nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "state launch");
+    }
+    return ok();
 }
 
 int ple_host_alloc(size_t bytes, void** host, void** device) {

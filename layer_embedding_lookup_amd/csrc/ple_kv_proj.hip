@@ -7,9 +7,10 @@
 // x [M][K] (gathered rows, K = H*D) and W [O][K] are both K-contiguous, so
 // every lane's MFMA operand (8 consecutive bf16 along K) is one 16-byte read
 // for both sides.  One pipelined kernel body, instantiated for 256 x 256
-// block tiles (problems with at least 256 of them) and 128 x 128 tiles
-// (decode and speculative-verify batches); its design is described above the
-// body.  Blocks are numbered so that the blocks resident on one XCD (block id
+// block tiles (problems with at least 256 of them), 128 x 128 tiles (a
+// 1024-token speculative-verify batch) and 64 x 64 tiles (decode batches);
+// its design is described above the body.  The block tile is the largest
+// that still gives 256 blocks, one per CU.  Blocks are numbered so that the blocks resident on one XCD (block id
 // mod 8 picks the XCD) work on neighbouring tiles and share their x and W
 // panels in that XCD's L2.
 #include "ple_launch.h"
@@ -42,14 +43,17 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
 // (BT/2) x (BT/2) block held in accumulator tiles of 32 x 32.  For BT = 256
 // that is 16 tiles (256 registers per lane, in the accumulation half of the
 // register file) and two LDS stages of 64 KiB; for BT = 128, 4 tiles and
-// stages of 32 KiB.  K-slices of 64.
+// stages of 32 KiB; for BT = 64, one tile and stages of 16 KiB.  K-slices
+// of 64.
 //
 // Why this shape: a wave's LDS traffic per MFMA falls as its block grows,
 // and 128 x 128 is the largest block whose accumulators fit one wave; the
 // fragment reads of the next 16-deep K-step are spread between the current
 // step's MFMAs, so with one wave per SIMD the matrix core stays fed without
-// a second wave to cover for it.  The 128-wide tile gives a 1024-token
-// batch 256 blocks, one per CU.
+// a second wave to cover for it.  The narrower tiles trade that for
+// blocks: a 1024-token batch gets 256 blocks of 128 x 128, a 256-token decode
+// batch 256 blocks of 64 x 64 (there the W panels, read by four blocks each
+// from the XCD's L2, bound the kernel, not the matrix cores).
 //
 // Operands go global -> LDS with buffer loads that write LDS directly
 // (buffer_load_dwordx4 ... lds): a scalar buffer resource per operand panel
@@ -80,9 +84,9 @@ constexpr int kBBK = 64;
 constexpr int kNStage = 2;
 constexpr int kBigMaxK = 1 << 20;  // keeps 256 rows of K bf16 within a 32-bit buffer offset
 
-// Block tile BT x BT (256, or 128 for problems too small to fill the chip
-// with 256-wide tiles); each of the 4 waves holds a (BT/2) x (BT/2) block as
-// NB x NB accumulator tiles of 32 x 32.
+// Block tile BT x BT (256, or 128 / 64 for problems too small to fill the
+// chip with wider tiles); each of the 4 waves holds a (BT/2) x (BT/2) block
+// as NB x NB accumulator tiles of 32 x 32.
 template <int BT>
 struct PipeShape {
     static constexpr int NB = BT / 64;                    // 32-row blocks per wave and operand
@@ -111,6 +115,7 @@ struct PipeFrag {
 #define PLE_FRAG_REGS4(f) \
     "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3])
 #define PLE_FRAG_REGS2(f) "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0]), "+v"(f.b[1])
+#define PLE_FRAG_REGS1(f) "+v"(f.a[0]), "+v"(f.b[0])
 
 template <int BT>
 __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M,
@@ -196,26 +201,35 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
                 case 6: asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(f.b[2]) : "v"(pb)); break;
                 default: asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(f.b[3]) : "v"(pb)); break;
             }
-        } else {
+        } else if constexpr (NB == 2) {
             switch (q) {
                 case 0: asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[0]) : "v"(pa)); break;
                 case 1: asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(f.a[1]) : "v"(pa)); break;
                 case 2: asm volatile("ds_read_b128 %0, %1" : "=v"(f.b[0]) : "v"(pb)); break;
                 default: asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(f.b[1]) : "v"(pb)); break;
             }
+        } else {
+            if (q == 0)
+                asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[0]) : "v"(pa));
+            else
+                asm volatile("ds_read_b128 %0, %1" : "=v"(f.b[0]) : "v"(pb));
         }
     };
     auto wait_frag = [&](Frag& f) {
         if constexpr (NB == 4)
             asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG_REGS4(f));
-        else
+        else if constexpr (NB == 2)
             asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG_REGS2(f));
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG_REGS1(f));
     };
     auto wait_barrier = [&](Frag& f) {
         if constexpr (NB == 4)
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG_REGS4(f) : : "memory");
-        else
+        else if constexpr (NB == 2)
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG_REGS2(f) : : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG_REGS1(f) : : "memory");
     };
     // One K-step: NB*NB MFMAs on `cur`.  After MFMA t < 2*NB comes fragment
     // read t of (rkt, rkk) into `nxt`, and copy instructions [c0, c1) of slice
@@ -229,7 +243,14 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
             acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur.b[j]),
                                                                 __builtin_bit_cast(bf16x8, cur.a[i]), acc[j][i], 0, 0,
                                                                 0);
-            if (rkk >= 0 && t < 2 * NB) read_one(t, rkt, rkk, nxt);
+            if (rkk >= 0) {
+                if constexpr (2 * NB <= NT) {
+                    if (t < 2 * NB) read_one(t, rkt, rkk, nxt);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2 * NB; ++q) read_one(q, rkt, rkk, nxt);  // NT == 1
+                }
+            }
             if (nc > 0 && (t * nc) % NT < nc) copy_one(ckt, c0 + (t * nc) / NT);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -295,6 +316,7 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
 }
 #undef PLE_FRAG_REGS4
 #undef PLE_FRAG_REGS2
+#undef PLE_FRAG_REGS1
 
 // The two block tiles as plain kernels (their bodies use device-only
 // builtins, which a kernel template would also instantiate for the host).
@@ -308,31 +330,43 @@ __global__ __launch_bounds__(kBigThreads, 1) void kv_proj_mid_kernel(const uint1
                                                                      int O, uint16_t* __restrict__ out) {
     kv_proj_pipe<128>(x, w, M, K, O, out);
 }
+__global__ __launch_bounds__(kBigThreads, 1) void kv_proj_small_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ w, int M, int K,
+                                                                       int O, uint16_t* __restrict__ out) {
+    kv_proj_pipe<64>(x, w, M, K, O, out);
+}
 
 template <int BT>
 static hipError_t launch_kv_proj_pipe(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                                       hipStream_t s) {
     using P = PipeShape<BT>;
-    const void* fn = BT == 256 ? (const void*)kv_proj_big_kernel : (const void*)kv_proj_mid_kernel;
+    const void* fn = BT == 256   ? (const void*)kv_proj_big_kernel
+                     : BT == 128 ? (const void*)kv_proj_mid_kernel
+                                 : (const void*)kv_proj_small_kernel;
     static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = (int)((M + BT - 1) / BT) * ((O + BT - 1) / BT);
     if (BT == 256)
         hipLaunchKernelGGL(kv_proj_big_kernel, dim3(tiles), dim3(kBigThreads), P::LDS_BYTES, s, x, w, (int)M, K, O,
                            kv);
-    else
+    else if (BT == 128)
         hipLaunchKernelGGL(kv_proj_mid_kernel, dim3(tiles), dim3(kBigThreads), P::LDS_BYTES, s, x, w, (int)M, K, O,
+                           kv);
+    else
+        hipLaunchKernelGGL(kv_proj_small_kernel, dim3(tiles), dim3(kBigThreads), P::LDS_BYTES, s, x, w, (int)M, K, O,
                            kv);
     return hipGetLastError();
 }
 
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s) {
-    // 256 x 256 tiles when they alone fill the chip; 128 x 128 otherwise
+    // the widest block tile that still gives 256 blocks
     if (K > kBigMaxK) return hipErrorInvalidValue;  // rejected by the argument checks before this
     const int64_t big_tiles = ((M + 255) / 256) * ((O + 255) / 256);
     if (big_tiles >= 256) return launch_kv_proj_pipe<256>(x, w, M, K, O, kv, s);
-    return launch_kv_proj_pipe<128>(x, w, M, K, O, kv, s);
+    const int64_t mid_tiles = ((M + 127) / 128) * ((O + 127) / 128);
+    if (mid_tiles >= 256) return launch_kv_proj_pipe<128>(x, w, M, K, O, kv, s);
+    return launch_kv_proj_pipe<64>(x, w, M, K, O, kv, s);
 }
 
 }  // namespace ple

@@ -55,9 +55,9 @@ hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, 
 hipError_t launch_conv_state_out(const uint16_t* x, const int32_t* qsl, int64_t T, int R,
                                  const uint16_t* state, int N, int S, uint16_t* state_out, hipStream_t s);
 
-// Speculative decode commit: carried conv state (state_out non-NULL, S > 0)
-// and n-gram context (ctx_out non-NULL, C > 0) for the first accepted[r]
-// tokens of each request window, both in one launch.
+// Carried conv state (state_out non-NULL, S > 0) and n-gram context (ctx_out
+// non-NULL, C > 0) in one launch: over each request's whole window, or with
+// accepted (speculative decode) over its first accepted[r] tokens.
 hipError_t launch_spec_commit(const int32_t* tok, const uint16_t* x, const int32_t* qsl, int64_t T, int R,
                               const int32_t* accepted, const uint16_t* state, int N, int S, uint16_t* state_out,
                               const int32_t* ctx, int C, int32_t eos, int32_t* ctx_out, hipStream_t s);

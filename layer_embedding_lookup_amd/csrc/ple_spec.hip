@@ -8,6 +8,9 @@
 // step starts from, as if only those tokens had been run: the same carried
 // rows as the plain state update, over the window cut to the accepted prefix.
 //
+// With accepted NULL the same kernel is the plain state update of a step (the
+// fused path uses it so that context and conv state cost one launch).
+//
 // One launch does both parts: wave w < R*S copies state row (w / S, w % S)
 // (one HBM read and one write per 16-byte chunk); the waves after it write
 // the context, one entry per lane.  Every wave has a fixed amount of work and

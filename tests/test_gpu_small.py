@@ -255,11 +255,11 @@ def _check_kv(got, want, x, w):
     assert (d > 0).mean() < 0.01
 
 
-@pytest.mark.parametrize("M,K,O", [# 128 x 128 tile kernel (< 256 tiles of 256 x 256), incl. one K-slice
+@pytest.mark.parametrize("M,K,O", [# 64 x 64 tile kernel (< 256 tiles of 128 x 128), incl. one K-slice
                                    (24, 128, 256), (1, 64, 16), (300, 192, 80), (129, 128, 144), (200, 64, 272),
-                                   (256, 2048, 4096), (1000, 512, 1024),
-                                   # the decode and speculative-verify widths, ragged in M and O
-                                   (1024, 2048, 4096), (1000, 2048, 4112),
+                                   (256, 2048, 4096), (1000, 512, 1024), (65, 64, 4096),
+                                   # 128 x 128 tiles: the speculative-verify width, ragged in M and O
+                                   (1024, 2048, 4096), (1000, 2048, 4112), (2048, 64, 2064),
                                    # 256 x 256 tile kernel (>= 256 tiles): 1 to 5 K-slices of 64,
                                    # ragged in M and in O
                                    (4100, 128, 4112), (4103, 256, 4096), (64, 64, 65536), (2048, 192, 8192),
