@@ -91,12 +91,17 @@ template <int BT>
 struct PipeShape {
     static constexpr int NB = BT / 64;                    // 32-row blocks per wave and operand
     static constexpr int NCOPY = BT / 32;                 // copy instructions per operand, wave and slice
-    static constexpr int COPY_SPLIT = NCOPY / 2;          // of those, issued in a slice's last K-step
+    static constexpr int COPY_SPLIT = NCOPY / 2;          // of those, issued in a slice's last K-step (2 stages)
     static constexpr int OP_BYTES = BT * kBBK * 2;        // one operand's slice (BT rows of 128 bytes)
     static constexpr int STAGE_BYTES = 2 * OP_BYTES;      // x + W slices
+    // LDS stages: the narrower tiles run fewer MFMAs per slice, so more
+    // slices are kept in flight to cover the copy latency (128 KiB each way)
+    static constexpr int NS = BT == 256 ? kNStage : (128 * 1024) / STAGE_BYTES;
     static constexpr int OUT_ROW = BT + 8;                // epilogue row (elements)
-    static constexpr int LDS_BYTES = (kNStage * STAGE_BYTES > BT * OUT_ROW * 2) ? kNStage * STAGE_BYTES
-                                                                                 : BT * OUT_ROW * 2;
+    static constexpr int LDS_BYTES = (NS * STAGE_BYTES > BT * OUT_ROW * 2) ? NS * STAGE_BYTES : BT * OUT_ROW * 2;
+    // copy instructions of one slice (both operands) per wave
+    static constexpr int SLICE_COPIES = 2 * NCOPY;
+    static_assert((NS & (NS - 1)) == 0 && (NS - 1) * SLICE_COPIES <= 63, "stages must fit the vmcnt counter");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -153,11 +158,11 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
         boff[i] = (uint32_t)((min(n0 + row, O - 1) - n0) * K * 2 + kc * 16);
     }
     const int nk = K / kBBK;
-    // copy instruction i of slice kt into stage kt % 2; slices past the end
+    // copy instruction i of slice kt into stage kt % NS; slices past the end
     // (the loop below is uniform) re-read the last slice into a stage that no
     // later read uses
     auto copy_one = [&](int kt, int i) {
-        char* base = lds_raw + (kt % kNStage) * P::STAGE_BYTES;
+        char* base = lds_raw + (kt & (P::NS - 1)) * P::STAGE_BYTES;
         const int g = i * 4 + wave;
         const int ko = min(kt, nk - 1) * kBBK * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(base + g * 1024), 16, aoff[i], ko, 0, 0);
@@ -188,7 +193,7 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
     }
     // fragment read q (0..2*NB-1) of K-step kk of slice kt: x blocks, then W blocks
     auto read_one = [&](int q, int kt, int kk, Frag& f) {
-        const uint32_t so = (uint32_t)(kt & 1) * P::STAGE_BYTES;
+        const uint32_t so = (uint32_t)(kt & (P::NS - 1)) * P::STAGE_BYTES;
         const uint32_t pa = a_addr[kk] + so, pb = b_addr[kk] + so;
         if constexpr (NB == 4) {
             switch (q) {
@@ -223,6 +228,15 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
         else
             asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG_REGS1(f));
     };
+    // the barrier of an NS-stage slice: this wave's copies of every slice but
+    // the next NS-2 have landed
+    auto wait_barrier_vm = [&](Frag& f) {
+        constexpr int V = (P::NS - 2) * P::SLICE_COPIES;
+        if constexpr (NB == 2)
+            asm volatile("s_waitcnt vmcnt(%4) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG_REGS2(f) : "i"(V) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%2) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG_REGS1(f) : "i"(V) : "memory");
+    };
     auto wait_barrier = [&](Frag& f) {
         if constexpr (NB == 4)
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG_REGS4(f) : : "memory");
@@ -251,7 +265,10 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
                     for (int q = 0; q < 2 * NB; ++q) read_one(q, rkt, rkk, nxt);  // NT == 1
                 }
             }
-            if (nc > 0 && (t * nc) % NT < nc) copy_one(ckt, c0 + (t * nc) / NT);
+            if (nc > 0 && nc <= NT && (t * nc) % NT < nc) copy_one(ckt, c0 + (t * nc) / NT);
+            if (nc > NT)
+#pragma unroll
+                for (int c = (t * nc) / NT; c < ((t + 1) * nc) / NT; ++c) copy_one(ckt, c0 + c);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -263,26 +280,52 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
     // the stage this slice has just left.  The last slice's look-ahead reads
     // and copies land in the other stage and are never used.
     auto slice = [&](int kt, Frag& f0, Frag& f1) {
-        wait_frag(f0);
-        kstep(f0, f1, kt, 1, kt + 1, P::COPY_SPLIT, P::NCOPY);
-        wait_frag(f1);
-        kstep(f1, f0, kt, 2, 0, 0, 0);
-        wait_frag(f0);
-        kstep(f0, f1, kt, 3, 0, 0, 0);
-        // every read of this stage is complete (all waves) and slice kt+1 has landed
-        __builtin_amdgcn_sched_barrier(0);
-        wait_barrier(f1);
-        __builtin_amdgcn_sched_barrier(0);
-        kstep(f1, f0, kt + 1, 0, kt + 2, 0, P::COPY_SPLIT);
+        if constexpr (P::NS == 2) {
+            wait_frag(f0);
+            kstep(f0, f1, kt, 1, kt + 1, P::COPY_SPLIT, P::NCOPY);
+            wait_frag(f1);
+            kstep(f1, f0, kt, 2, 0, 0, 0);
+            wait_frag(f0);
+            kstep(f0, f1, kt, 3, 0, 0, 0);
+            // every read of this stage is complete (all waves) and slice kt+1 has landed
+            __builtin_amdgcn_sched_barrier(0);
+            wait_barrier(f1);
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(f1, f0, kt + 1, 0, kt + 2, 0, P::COPY_SPLIT);
+        } else {
+            // NS stages: slices kt+1 .. kt+NS-1 are in flight or landed; after
+            // the barrier (this wave's copies of slice kt+1 done, every read of
+            // slice kt done) the last K-step refills slice kt's stage with
+            // slice kt+NS
+            wait_frag(f0);
+            kstep(f0, f1, kt, 1, 0, 0, 0);
+            wait_frag(f1);
+            kstep(f1, f0, kt, 2, 0, 0, 0);
+            wait_frag(f0);
+            kstep(f0, f1, kt, 3, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_barrier_vm(f1);
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(f1, f0, kt + 1, 0, kt + P::NS, 0, P::NCOPY);
+        }
     };
 
-    // slice 0 whole, then the first part of slice 1
-#pragma unroll
-    for (int i = 0; i < P::NCOPY; ++i) copy_one(0, i);
-    PLE_WAIT_VM_BARRIER0();
-#pragma unroll
-    for (int i = 0; i < P::COPY_SPLIT; ++i) copy_one(1, i);
     Frag f0, f1;
+    if constexpr (P::NS == 2) {
+        // slice 0 whole, then the first part of slice 1
+#pragma unroll
+        for (int i = 0; i < P::NCOPY; ++i) copy_one(0, i);
+        PLE_WAIT_VM_BARRIER0();
+#pragma unroll
+        for (int i = 0; i < P::COPY_SPLIT; ++i) copy_one(1, i);
+    } else {
+        // slices 0 .. NS-1, then wait for slice 0
+#pragma unroll
+        for (int k = 0; k < P::NS; ++k)
+#pragma unroll
+            for (int i = 0; i < P::NCOPY; ++i) copy_one(k, i);
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"((P::NS - 1) * P::SLICE_COPIES) : "memory");
+    }
 #pragma unroll
     for (int q = 0; q < 2 * NB; ++q) read_one(q, 0, 0, f0);
     for (int kt = 0; kt < nk; ++kt) slice(kt, f0, f1);
@@ -364,8 +407,10 @@ hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K
     if (K > kBigMaxK) return hipErrorInvalidValue;  // rejected by the argument checks before this
     const int64_t big_tiles = ((M + 255) / 256) * ((O + 255) / 256);
     if (big_tiles >= 256) return launch_kv_proj_pipe<256>(x, w, M, K, O, kv, s);
+    // (64-wide tiles take 128 KiB of LDS, so only while one block per CU covers them)
     const int64_t mid_tiles = ((M + 127) / 128) * ((O + 127) / 128);
-    if (mid_tiles >= 256) return launch_kv_proj_pipe<128>(x, w, M, K, O, kv, s);
+    const int64_t small_tiles = ((M + 63) / 64) * ((O + 63) / 64);
+    if (mid_tiles >= 256 || small_tiles > 256) return launch_kv_proj_pipe<128>(x, w, M, K, O, kv, s);
     return launch_kv_proj_pipe<64>(x, w, M, K, O, kv, s);
 }
 
