@@ -13,6 +13,9 @@
 // request's start come from the carried state.
 #include "ple_launch.h"
 
+#include <map>
+#include <mutex>
+
 #ifndef PLE_CONV_TOKENS_PER_BLOCK
 #define PLE_CONV_TOKENS_PER_BLOCK 32
 #endif
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     const int64_t t_begin = xcd * per_xcd;
     const int64_t t_end = min(T, t_begin + per_xcd);
     const int64_t stride = blocks_per_xcd * 4;
-    constexpr int CPL = 4;  // 16-byte chunks per lane per pass
+    constexpr int CPL = 2;  // 16-byte chunks per lane per pass (2 beat 1, 4 and 8 on gfx950)
 
     for (int64_t t = t_begin + (int64_t)(blockIdx.x >> 3) * 4 + wv; t < t_end; t += stride) {
         int r = 0;
@@ -469,12 +472,25 @@ static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_
     static const hipError_t attr = hipFuncSetAttribute((const void*)conv_rows_kernel<KC>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (attr != hipSuccess) return attr;
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC>, 256, lds) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    int64_t blocks = (int64_t)cus * per_cu;                  // every block resident at once
+    // resident blocks per device for this kernel and weight size (queried once)
+    static std::mutex mu;
+    static std::map<std::pair<int, size_t>, int64_t> resident;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int64_t blocks;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = resident.find({dev, lds});
+        if (it == resident.end()) {
+            int cus = 256, per_cu = 1;
+            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC>, 256, lds) != hipSuccess ||
+                per_cu < 1)
+                per_cu = 1;
+            it = resident.emplace(std::make_pair(dev, lds), (int64_t)cus * per_cu).first;
+        }
+        blocks = it->second;                                 // every block resident at once
+    }
     const int64_t need = (T + 3) / 4;                        // one wave per token at most
     if (blocks > need) blocks = need;
     blocks = ((blocks + 7) / 8) * 8;                         // whole XCD rounds
