@@ -87,12 +87,20 @@ int validate_hash(const ple_hash_desc* h, HashParams* hp) {
         if (off < 0 || off + V > ((int64_t)1 << 31))
             return fail(PLE_ERR_UNSUPPORTED, "head %d rows [%lld, %lld) do not fit int32 row ids", k,
                         (long long)off, (long long)(off + V));
-        hp->vocab[k] = (uint32_t)V;
-        hp->offset[k] = (uint32_t)off;
-        hp->barrett[k] = UINT64_MAX / (uint64_t)V;
-        hp->wrap_mod[k] = (uint32_t)((UINT64_MAX % (uint64_t)V + 1u) % (uint64_t)V);
-        hp->order[k] = (uint8_t)(2 + (h->first_head + k) / h->heads_per_ngram);
-        for (int j = 0; j < W; ++j) hp->mult[k][j] = (uint64_t)h->multipliers[(int64_t)k * W + j];
+        HeadHash& hh = hp->head[k];
+        hh.vocab = (uint32_t)V;
+        hh.offset = (uint32_t)off;
+        hh.barrett = UINT64_MAX / (uint64_t)V;
+        hh.wrap_mod = (uint32_t)((UINT64_MAX % (uint64_t)V + 1u) % (uint64_t)V);
+        hh.order = (uint32_t)(2 + (h->first_head + k) / h->heads_per_ngram);
+        // shifts at or beyond the head's order contribute nothing (zero multiplier)
+        for (int j = 0; j < W; ++j) {
+            const uint64_t m = j < (int)hh.order ? (uint64_t)h->multipliers[(int64_t)k * W + j] : 0u;
+            if (j < 4)
+                hh.mult[j] = m;
+            else
+                hp->mult_hi[k][j - 4] = m;
+        }
     }
     return PLE_OK;
 }

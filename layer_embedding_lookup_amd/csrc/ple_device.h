@@ -20,14 +20,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Per-call hash constants, passed by value as a kernel argument so that calls
 // on different streams (a prefetch for the next layer beside the current one)
-// never share mutable state.
+// never share mutable state.  One 64-byte record per head holds what every
+// order up to 4 needs (kernels stage the records of 16 heads with one 16-byte
+// load per lane); the multipliers of shifts 4..7 sit apart.
+struct alignas(16) HeadHash {
+    uint64_t mult[4];   // multiplier of shift j < 4; zero for j >= the head's order
+    uint64_t barrett;   // floor((2^64 - 1) / V_h)
+    uint32_t vocab;     // V_h < 2^31
+    uint32_t wrap_mod;  // 2^64 mod V_h
+    uint32_t offset;    // offsets[h]
+    uint32_t order;     // n-gram order of head h (2..C+1)
+    uint64_t pad;
+};
+static_assert(sizeof(HeadHash) == 64, "HeadHash is four 16-byte chunks");
+
 struct HashParams {
-    uint64_t mult[PLE_MAX_HEADS][PLE_MAX_CONTEXT + 1];
-    uint64_t barrett[PLE_MAX_HEADS];   // floor((2^64 - 1) / V_h)
-    uint32_t vocab[PLE_MAX_HEADS];     // V_h < 2^31
-    uint32_t wrap_mod[PLE_MAX_HEADS];  // 2^64 mod V_h
-    uint32_t offset[PLE_MAX_HEADS];    // offsets[h]
-    uint8_t order[PLE_MAX_HEADS];      // n-gram order of head h (2..C+1)
+    HeadHash head[PLE_MAX_HEADS];
+    uint64_t mult_hi[PLE_MAX_HEADS][PLE_MAX_CONTEXT + 1 - 4];  // shifts 4..7 (context_len >= 4 only)
     int32_t num_heads;
     int32_t context_len;
     int32_t eos;
@@ -85,46 +94,61 @@ __device__ __forceinline__ uint32_t floor_mod_wrapped(uint64_t acc, uint32_t V, 
     return rr;
 }
 
+// query_start_loc entries a wave holds for finding requests: entry
+// 1 + c*64 + lane in q[c] (all of qsl[0..R] in lane order when R + 1 <= 64,
+// then q[0] = qsl[lane]).  Loading is split from the search so that callers
+// can put these loads in flight together with their other first loads.
+struct QslProbe {
+    int q[16];
+};
+
+__device__ __forceinline__ void qsl_probe_load(const int32_t* __restrict__ qsl, int R, int lane, QslProbe& p) {
+    if (R + 1 <= kWave) {
+        p.q[0] = lane <= R ? qsl[lane] : 0;
+    } else if (R <= 16 * kWave) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int idx = 1 + c * kWave + lane;
+            p.q[c] = (idx <= R) ? qsl[idx] : 0;
+        }
+    }
+}
+
 // Request index r and clamped start a of token t (this lane's token, the
-// k-th of the wave's `ntok` consecutive tokens starting at t_first).  The wave
-// loads query_start_loc cooperatively (one load per lane per 64 entries, all
-// in flight together) and counts the entries <= each token with ballots, so
-// finding the request costs one memory round trip instead of a chain of
-// dependent binary-search loads.  Every lane of the wave must call this.
-__device__ __forceinline__ void wave_find_request(const int32_t* __restrict__ qsl, int R, int64_t t,
-                                                  int64_t t_first, int ntok, int my_k, int lane, int& r_out,
-                                                  int64_t& a_out) {
+// k-th of the wave's `ntok` consecutive tokens starting at t_first), from the
+// entries qsl_probe_load fetched: the wave counts the entries <= each token
+// with ballots, so finding the request costs the one round trip of the probe
+// instead of a chain of dependent binary-search loads (more than 1024
+// requests fall back to a binary search).  Every lane of the wave must call
+// this.
+__device__ __forceinline__ void wave_find_request_probed(const int32_t* __restrict__ qsl, const QslProbe& p, int R,
+                                                         int64_t t, int64_t t_first, int ntok, int my_k, int lane,
+                                                         int& r_out, int64_t& a_out) {
     int r;
     int64_t a;
     if (R + 1 <= kWave) {
-        const int q = lane <= R ? qsl[lane] : 0;
+        const int q = p.q[0];
         r = 0;
         for (int k = 0; k < ntok; ++k) {
             const int64_t tk = t_first + k;
             const uint64_t m = __ballot(lane >= 1 && lane <= R && (int64_t)q <= tk);
-            const int rk = min(__popcll(m), R - 1);
-            if (k == my_k) r = rk;
+            const int rk = (int)__popcll(m);
+            if (k == my_k) r = rk < R - 1 ? rk : R - 1;
         }
         a = __shfl(q, r, kWave);
     } else if (R <= 16 * kWave) {
-        int q[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int idx = 1 + c * kWave + lane;
-            q[c] = (idx <= R) ? qsl[idx] : 0;
-        }
         int cnt = 0;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             const int idx = 1 + c * kWave + lane;
             if (1 + c * kWave <= R) {  // wave-uniform
                 for (int k = 0; k < ntok; ++k) {
-                    const uint64_t m = __ballot(idx <= R && (int64_t)q[c] <= t_first + k);
-                    if (k == my_k) cnt += __popcll(m);
+                    const uint64_t m = __ballot(idx <= R && (int64_t)p.q[c] <= t_first + k);
+                    if (k == my_k) cnt += (int)__popcll(m);
                 }
             }
         }
-        r = min(cnt, R - 1);
+        r = cnt < R - 1 ? cnt : R - 1;
         a = qsl[r];
     } else {
         r = find_request(qsl, R, t);
@@ -132,6 +156,14 @@ __device__ __forceinline__ void wave_find_request(const int32_t* __restrict__ qs
     }
     r_out = r;
     a_out = a < 0 ? 0 : (a > t ? t : a);  // keeps every read in bounds for any qsl
+}
+
+__device__ __forceinline__ void wave_find_request(const int32_t* __restrict__ qsl, int R, int64_t t,
+                                                  int64_t t_first, int ntok, int my_k, int lane, int& r_out,
+                                                  int64_t& a_out) {
+    QslProbe p;
+    qsl_probe_load(qsl, R, lane, p);
+    wave_find_request_probed(qsl, p, R, t, t_first, ntok, my_k, lane, r_out, a_out);
 }
 
 // Tokens of request r that the carried state and context take in: [a, b) =

@@ -20,9 +20,10 @@
 // Waves never wait for each other.
 #include "ple_launch.h"
 
-// Tuning knobs (compile-time): 16-byte loads in flight per lane, and whether
-// table reads / row writes carry the non-temporal hint.
-// Output chunks (16 bytes) per lane per pass, by table format.
+// Tuning knobs (compile-time): 16-byte output chunks per lane per pass by
+// table format, non-temporal row stores by table format (measured: the
+// expanding fp8 and NVFP4 stores gain from them, plain bf16 copies do not),
+// and which stream bf16 rows take (0: per-lane, 1: scalar-address).
 #ifndef PLE_LOOKUP_LOADS
 #define PLE_LOOKUP_LOADS 16
 #endif
@@ -32,11 +33,17 @@
 #ifndef PLE_LOOKUP_LOADS_FP4
 #define PLE_LOOKUP_LOADS_FP4 16
 #endif
-#ifndef PLE_LOOKUP_NT_LOAD
-#define PLE_LOOKUP_NT_LOAD 1
+#ifndef PLE_LOOKUP_NT_STORE_BF16
+#define PLE_LOOKUP_NT_STORE_BF16 0
 #endif
-#ifndef PLE_LOOKUP_NT_STORE
-#define PLE_LOOKUP_NT_STORE 0
+#ifndef PLE_LOOKUP_NT_STORE_QUANT
+#define PLE_LOOKUP_NT_STORE_QUANT 1
+#endif
+#ifndef PLE_LOOKUP_BF16_SCALAR_ROWS
+#define PLE_LOOKUP_BF16_SCALAR_ROWS 0
+#endif
+#ifndef PLE_LOOKUP_QUANT_SCALAR_ROWS
+#define PLE_LOOKUP_QUANT_SCALAR_ROWS 1
 #endif
 #ifndef PLE_LOOKUP_BLOCK
 #define PLE_LOOKUP_BLOCK 256  // threads per block; waves are independent
@@ -90,116 +97,186 @@ __device__ __forceinline__ u32x4 dequant8_fp4(uint32_t q, uint32_t bcode, float 
                  pack_bf16x2_canon((v3.x * s) * tscale, (v3.y * s) * tscale)};
 }
 
-// ID of head h for token t, given its request (r, a) and the raw tokens
-// w[j] = tok[max(t-j, 0)] loaded ahead (the value is used only when t-j >= a).
-__device__ __forceinline__ int32_t window_id(const HashParams& hp, const int32_t (&w)[PLE_MAX_CONTEXT + 1],
-                                             const int32_t* __restrict__ ctx, int r, int64_t a, int64_t t, int h) {
+// Everything a lane needs for the ID of its (token t, head h) pair apart from
+// the request boundaries: the raw tokens w[j] = tok[max(t-j, 0)] for shifts
+// j <= C (a value is used only when t-j lies in the token's request) and
+// head h's constants.
+struct IdInputs {
+    int32_t w[PLE_MAX_CONTEXT + 1];
+    uint64_t m[PLE_MAX_CONTEXT + 1];
+    uint64_t barrett;
+    uint32_t vocab, wrap_mod, offset, order;
+};
+
+// The head records reach each lane through LDS.  A wave loads the records of
+// heads 0..15 (1 KiB, one 16-byte chunk per lane) straight from the kernel
+// argument block at entry: the load needs only the block's address, so it is
+// in flight together with the kernel's first scalar argument loads, and the
+// records cost no round trip of their own.  Heads 16..31 (more than 16 heads
+// in a call) follow once the head count is known.
+struct HeadStage {
+    u32x4 lo;  // chunk `lane` of head records 0..15
+};
+
+__device__ __forceinline__ void head_stage_load(const HashParams& hp, int lane, HeadStage& st) {
+    st.lo = ((const u32x4*)&hp.head[0])[lane];
+}
+
+// The wave's stage holds 128 chunks (32 records); id_consts_read reads them.
+__device__ __forceinline__ void head_stage_store(const HashParams& hp, const HeadStage& st, int H, int lane,
+                                                 u32x4* __restrict__ lds) {
+    lds[lane] = st.lo;
+    if (H > 16) lds[kWave + lane] = ((const u32x4*)&hp.head[0])[kWave + lane];  // wave-uniform
+}
+
+// The token window comes from memory (t clamped into the batch, for waves
+// past its end), the head record from the wave's LDS stage; the first only
+// issues loads, so that they share one round trip with the query_start_loc
+// load and the stage's own load.
+__device__ __forceinline__ void id_tokens_load(const HashParams& hp, const int32_t* __restrict__ tok, int64_t T,
+                                               int64_t t, IdInputs& in) {
     const int C = hp.context_len;
-    const int32_t eos = hp.eos;
-    const int order = hp.order[h];
-    uint64_t acc = (uint64_t)(int64_t)w[0] * hp.mult[h][0];
+    const int64_t tc = t < T ? t : T - 1;
+#pragma unroll
+    for (int j = 0; j <= PLE_MAX_CONTEXT; ++j) {
+        const int64_t p = tc - (j <= C ? j : C);
+        in.w[j] = tok[p >= 0 ? p : 0];
+    }
+}
+
+__device__ __forceinline__ void id_consts_read(const HashParams& hp, const u32x4* __restrict__ lds, int h,
+                                               IdInputs& in) {
+    const int C = hp.context_len;
+    __builtin_amdgcn_wave_barrier();  // the record reads follow the wave's own LDS writes
+    const u32x4 c0 = lds[4 * h], c1 = lds[4 * h + 1], c2 = lds[4 * h + 2], c3 = lds[4 * h + 3];
+    in.m[0] = (uint64_t)c0.y << 32 | c0.x;
+    in.m[1] = (uint64_t)c0.w << 32 | c0.z;
+    in.m[2] = (uint64_t)c1.y << 32 | c1.x;
+    in.m[3] = (uint64_t)c1.w << 32 | c1.z;
+#pragma unroll
+    for (int j = 4; j <= PLE_MAX_CONTEXT; ++j) in.m[j] = C >= 4 ? hp.mult_hi[h][j - 4] : 0u;  // wave-uniform
+    in.barrett = (uint64_t)c2.y << 32 | c2.x;
+    in.vocab = c2.z;
+    in.wrap_mod = c2.w;
+    in.offset = c3.x;
+    in.order = c3.y;
+}
+
+// ID of the lane's (token t, head h) pair in request r starting at a:
+// shifts before the request start read the carried context (oldest first)
+// or EOS; once a shift reads EOS every older shift reads EOS (the current
+// token never masks); the wrapped 64-bit sum of token x multiplier is
+// reduced by a signed floor modulo and offset into the head's rows.
+__device__ __forceinline__ int32_t window_id(const IdInputs& in, int C, int32_t eos,
+                                             const int32_t* __restrict__ ctx, int r, int64_t a, int64_t t) {
+    // raw tokens of shifts 1..C first (the context reads all in flight), then the sum
+    int32_t raw[PLE_MAX_CONTEXT + 1];
+#pragma unroll
+    for (int j = 1; j <= PLE_MAX_CONTEXT; ++j) {
+        raw[j] = in.w[j];
+        if (j <= C && j < (int)in.order) {
+            const int64_t p = t - j;
+            if (p < a) raw[j] = ctx != nullptr ? ctx[(int64_t)r * C + (C - (a - p))] : eos;
+        }
+    }
+    uint64_t acc = (uint64_t)(int64_t)in.w[0] * in.m[0];
     bool crossed = false;
 #pragma unroll
     for (int j = 1; j <= PLE_MAX_CONTEXT; ++j) {
-        if (j < order) {
-            const int64_t p = t - j;
-            int32_t raw;
-            if (p >= a)
-                raw = w[j];
-            else if (ctx != nullptr)
-                raw = ctx[(int64_t)r * C + (C - (a - p))];
-            else
-                raw = eos;
-            crossed |= (raw == eos);
-            const int64_t sj = crossed ? (int64_t)eos : (int64_t)raw;
-            acc += (uint64_t)sj * hp.mult[h][j];
+        if (j <= C && j < (int)in.order) {
+            crossed |= (raw[j] == eos);
+            const int64_t sj = crossed ? (int64_t)eos : (int64_t)raw[j];
+            acc += (uint64_t)sj * in.m[j];
         }
     }
-    return (int32_t)(hp.offset[h] + floor_mod_wrapped(acc, hp.vocab[h], hp.barrett[h], hp.wrap_mod[h]));
+    return (int32_t)(in.offset + floor_mod_wrapped(acc, in.vocab, in.barrett, in.wrap_mod));
 }
 
-__device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
-#if PLE_LOOKUP_NT_STORE
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+// pointer into global memory (address space 1) from a 64-bit address, so that
+// loads through it are global, not flat, instructions
+template <typename T>
+using gptr = const T __attribute__((address_space(1)))*;
+
+// 64-bit value of lane `l` for every lane
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, l, kWave);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), l, kWave);
+    return (uint64_t)hi << 32 | lo;
 }
 
-// One wave: `tokens_per_wave` consecutive tokens x H heads = at most 64 rows,
-// one lane per (token, head) pair for the IDs.  No block-level barrier: each
-// wave computes its IDs and streams its rows on its own.  MODE_HASH computes
-// the IDs, MODE_IDS reads (and clamps) caller IDs.
+// 64-bit value of lane `l` (wave-uniform) as a scalar
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return (uint64_t)hi << 32 | lo;
+}
+
+// What both row streams need: every lane produces one 16-byte output chunk
+// (8 bf16 elements) per step, so stores are always lane-contiguous; its input
+// is the same 8 elements of the stored row: 16 bytes (bf16), 8 (fp8 codes) or
+// 4 (NVFP4 codes, plus the block's scale code).
+struct StreamArgs {
+    const char* table;
+    uint16_t* out;  // the wave's [rows][dim] output slab
+    int cpr;        // 16-byte output chunks per row
+    int shift;      // log2(cpr), or -1
+    int nrows;
+    int total;      // nrows * cpr
+};
+
+__device__ __forceinline__ StreamArgs stream_args(const LookupArgs& g, int64_t t0, int nrows) {
+    StreamArgs a;
+    a.table = (const char*)g.table;
+    a.out = g.rows + t0 * g.num_heads * (int64_t)g.dim;
+    a.cpr = g.dim >> 3;
+    a.shift = g.cpr_log2;
+    a.nrows = nrows;
+    a.total = nrows * a.cpr;
+    return a;
+}
+
+template <int DTYPE>
+constexpr int in_bytes() {  // input bytes per output chunk
+    return DTYPE == kFmtBF16 ? 16 : (DTYPE == kFmtFP8 ? 8 : 4);
+}
+
+__device__ __forceinline__ void store16(u32x4* p, u32x4 v, bool nt) {
+    if (nt)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+// Per-lane stream (any row length): chunk idx = base + u*64 + lane of the
+// wave's slab belongs to row idx / cpr, whose ID the lane reads from the
+// row's owning lane; up to UNROLL loads per lane in flight, then the stores.
+// bf16 tables take this stream by default: for plain row copies it measured
+// faster than the scalar-address stream below.
 template <int DTYPE, int MODE, int UNROLL>
-__global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp, LookupArgs g) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = (int64_t)blockIdx.x * (PLE_LOOKUP_BLOCK / kWave) + (threadIdx.x >> 6);
-    const int TW = g.tokens_per_wave;
-    const int64_t t0 = wave * TW;
-    if (t0 >= g.num_tokens) return;  // whole wave
-    const int H = g.num_heads;
-    const int nt = (int)min((int64_t)TW, g.num_tokens - t0);
-    const int nrows = nt * H;
-    const bool active = lane < nrows;
-    const int my_k = active ? lane / H : 0;
-    const int h = active ? lane - my_k * H : 0;
-    const int64_t t = t0 + my_k;
-
-    int32_t id = 0;
-    if (MODE == kModeHash) {
-        int32_t w[PLE_MAX_CONTEXT + 1];
-#pragma unroll
-        for (int j = 0; j <= PLE_MAX_CONTEXT; ++j)
-            w[j] = (j <= hp.context_len) ? g.tok[t - j >= 0 ? t - j : 0] : 0;
-        int r;
-        int64_t a;
-        wave_find_request(g.qsl, g.num_reqs, t, t0, nt, my_k, lane, r, a);
-        id = window_id(hp, w, g.ctx, r, a, t, h);
-        if (active && g.ids_out != nullptr) g.ids_out[t0 * H + lane] = id;
-    } else {
-        id = active ? g.ids_in[t0 * H + lane] : 0;
-        id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
-    }
-    // ids mode with rep_of: a repeated row is left for a later copy
-    int skip = 0;
-    if (MODE == kModeIds && g.rep_of != nullptr && active) skip = g.rep_of[t0 * H + lane] != (int32_t)(t0 * H + lane);
+__device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const StreamArgs& a, int id, int skip,
+                                                 float tscale, int lane) {
+    constexpr int IB = in_bytes<DTYPE>();
+    const int64_t row_bytes = (int64_t)a.cpr * IB;
     float scale = 0.f;
     if (DTYPE == kFmtFP8) scale = g.scales[(int64_t)id * g.scale_stride];
-    const float tscale = DTYPE == kFmtNVFP4 ? g.scales[0] : 0.f;
-
-    // Every lane produces one 16-byte output chunk (8 bf16 elements) per
-    // step, so stores are always lane-contiguous; its input is the same 8
-    // elements of the stored row: 16 bytes (bf16), 8 (fp8 codes) or 4 (NVFP4
-    // codes, plus the block's scale code).
-    const int cpr = g.dim >> 3;    // output chunks per row
-    const int shift = g.cpr_log2;  // >= 0 when cpr is a power of two
-    const int total = nrows * cpr;
-    const char* __restrict__ table = (const char*)g.table;
-    constexpr int IB = DTYPE == kFmtBF16 ? 16 : (DTYPE == kFmtFP8 ? 8 : 4);  // input bytes per chunk
-    const int64_t row_bytes = (int64_t)cpr * IB;
-    u32x4* __restrict__ out = (u32x4*)(g.rows + t0 * H * (int64_t)g.dim);
-
-    for (int base = 0; base < total; base += kWave * UNROLL) {
+    u32x4* __restrict__ out = (u32x4*)a.out;
+    for (int base = 0; base < a.total; base += kWave * UNROLL) {
         u32x4 v[UNROLL];
         float sc[UNROLL];
         uint32_t bsc[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + u * kWave + lane;
-            int row = shift >= 0 ? (idx >> shift) : (idx / cpr);
-            row = row < nrows ? row : nrows - 1;
+            int row = a.shift >= 0 ? (idx >> a.shift) : (idx / a.cpr);
+            row = row < a.nrows ? row : a.nrows - 1;
             const int rid = __shfl(id, row, kWave);
             if (DTYPE == kFmtFP8) sc[u] = __shfl(scale, row, kWave);
             const int rskip = MODE == kModeIds ? __shfl(skip, row, kWave) : 0;
-            if (idx < total && !rskip) {
-                const int ch = idx - row * cpr;
-                const char* src = table + (int64_t)rid * row_bytes + (int64_t)ch * IB;
+            if (idx < a.total && !rskip) {
+                const int ch = idx - row * a.cpr;
+                const char* src = a.table + (int64_t)rid * row_bytes + (int64_t)ch * IB;
                 if (DTYPE == kFmtBF16) {
-#if PLE_LOOKUP_NT_LOAD
                     v[u] = __builtin_nontemporal_load((const u32x4*)src);
-#else
-                    v[u] = *(const u32x4*)src;
-#endif
                 } else if (DTYPE == kFmtFP8) {
                     const u32x2 q = __builtin_nontemporal_load((const u32x2*)src);
                     v[u] = u32x4{q.x, q.y, 0u, 0u};
@@ -214,19 +291,151 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
             const int idx = base + u * kWave + lane;
             int rskip = 0;
             if (MODE == kModeIds) {
-                int row = shift >= 0 ? (idx >> shift) : (idx / cpr);
-                rskip = __shfl(skip, row < nrows ? row : nrows - 1, kWave);
+                const int row = a.shift >= 0 ? (idx >> a.shift) : (idx / a.cpr);
+                rskip = __shfl(skip, row < a.nrows ? row : a.nrows - 1, kWave);
             }
-            if (idx < total && !rskip) {
+            if (idx < a.total && !rskip) {
                 if (DTYPE == kFmtBF16)
-                    store16(out + idx, v[u]);
+                    store16(out + idx, v[u], PLE_LOOKUP_NT_STORE_BF16);
                 else if (DTYPE == kFmtFP8)
-                    store16(out + idx, dequant8_fp8(v[u].x, v[u].y, sc[u]));
+                    store16(out + idx, dequant8_fp8(v[u].x, v[u].y, sc[u]), PLE_LOOKUP_NT_STORE_QUANT);
                 else
-                    store16(out + idx, dequant8_fp4(v[u].x, bsc[u], tscale));
+                    store16(out + idx, dequant8_fp4(v[u].x, bsc[u], tscale), PLE_LOOKUP_NT_STORE_QUANT);
             }
         }
     }
+}
+
+// Scalar-address stream, for rows of 64 x 2^k output chunks: every pass of 64
+// chunks then lies in one row.  Lane u first works out pass u's source
+// address and store offset with a few vector operations for all passes at
+// once (the row's base address fetched from the lane that owns the row); each
+// load then takes them by lane reads into scalar registers, so the loads go
+// out back to back from scalar bases.  The wave's output slab is a buffer
+// resource: a store at an offset past its end is dropped by the hardware,
+// which masks the ragged tail and the skipped rows without a branch (a
+// branch around each store lets the compiler sink the loads into it).
+template <int DTYPE, int MODE, int UNROLL>
+__device__ __forceinline__ void stream_rows_scalar(const LookupArgs& g, const StreamArgs& a, int id, int skip,
+                                                   float tscale, int lane) {
+    constexpr int IB = in_bytes<DTYPE>();
+    const int64_t row_bytes = (int64_t)a.cpr * IB;
+    const __amdgpu_buffer_rsrc_t orsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.out, (short)0, a.total * 16, 0x00020000);
+    // per lane (one row each): the row's address, its fp8 scale (loaded now,
+    // used at the dequant) and its NVFP4 block-scale address
+    const uint64_t my_row = (uint64_t)a.table + (uint64_t)(uint32_t)id * (uint64_t)row_bytes;
+    float my_scale = 0.f;
+    uint64_t my_bs = 0;
+    if (DTYPE == kFmtFP8) my_scale = g.scales[(int64_t)id * g.scale_stride];
+    if (DTYPE == kFmtNVFP4) my_bs = (uint64_t)g.block_scales + (uint64_t)(uint32_t)id * (uint64_t)(g.dim >> 4);
+    const int lppr = a.shift - 6;  // log2(passes per row)
+    const bool nt = DTYPE == kFmtBF16 ? PLE_LOOKUP_NT_STORE_BF16 : PLE_LOOKUP_NT_STORE_QUANT;
+    for (int base = 0; base < a.total; base += kWave * UNROLL) {
+        // pass P = base/64 + lane covers chunks [cp*64, cp*64 + 64) of row P >> lppr
+        const int P = (base >> 6) + lane;
+        const int prow = P >> lppr;
+        const int pcp = P & ((1 << lppr) - 1);
+        const int prowc = prow < a.nrows ? prow : a.nrows - 1;
+        const uint64_t paddr = shfl64(my_row, prowc) + (uint64_t)(pcp * kWave * IB);
+        const int pskip = MODE == kModeIds ? __shfl(skip, prowc, kWave) : 0;
+        const int psoff = (prow < a.nrows && !pskip) ? (prow * a.cpr + pcp * kWave) * 16 : a.total * 16;
+        uint64_t pbs = 0;
+        if (DTYPE == kFmtNVFP4) pbs = shfl64(my_bs, prowc) + (uint64_t)(pcp * kWave / 2);
+        u32x4 v[UNROLL];
+        uint32_t bsc[UNROLL];
+        int soff[UNROLL], rsel[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            soff[u] = __builtin_amdgcn_readlane(psoff, u);
+            rsel[u] = DTYPE == kFmtFP8 ? __builtin_amdgcn_readlane(prowc, u) : 0;
+            // computed IDs always load (the address is a valid row); caller IDs
+            // skip the repeated rows
+            if (MODE == kModeHash || soff[u] < a.total * 16) {
+                const uint64_t rb = readlane64(paddr, u);
+                if (DTYPE == kFmtBF16) {
+                    v[u] = __builtin_nontemporal_load((gptr<u32x4>)rb + lane);
+                } else if (DTYPE == kFmtFP8) {
+                    const u32x2 q = __builtin_nontemporal_load((gptr<u32x2>)rb + lane);
+                    v[u] = u32x4{q.x, q.y, 0u, 0u};
+                } else {
+                    v[u] = u32x4{__builtin_nontemporal_load((gptr<uint32_t>)rb + lane), 0u, 0u, 0u};
+                    bsc[u] = ((gptr<uint8_t>)readlane64(pbs, u))[lane >> 1];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            u32x4 o;
+            if (DTYPE == kFmtBF16) {
+                o = v[u];
+            } else if (DTYPE == kFmtFP8) {
+                const float s = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_scale), rsel[u]));
+                o = dequant8_fp8(v[u].x, v[u].y, s);
+            } else {
+                o = dequant8_fp4(v[u].x, bsc[u], tscale);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, lane * 16, soff[u], nt ? 2 : 0);
+        }
+    }
+}
+
+// One wave: `tokens_per_wave` consecutive tokens x H heads = at most 64 rows,
+// one lane per (token, head) pair for the IDs.  No block-level barrier: each
+// wave computes its IDs and streams its rows on its own.  MODE_HASH computes
+// the IDs, MODE_IDS reads (and clamps) caller IDs.
+template <int DTYPE, int MODE, int UNROLL, bool SCALAR_ROWS>
+__global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp, LookupArgs g) {
+    __shared__ u32x4 head_lds[PLE_LOOKUP_BLOCK / kWave][2 * kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    HeadStage hst;
+    if (MODE == kModeHash) head_stage_load(hp, lane, hst);
+    // the wave index is uniform; saying so keeps everything derived from it
+    // (token range, row count, output slab) in scalar registers
+    const int64_t wave = (int64_t)blockIdx.x * (PLE_LOOKUP_BLOCK / kWave) +
+                         __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int TW = g.tokens_per_wave;
+    const int64_t t0 = wave * TW;
+    const bool live = t0 < g.num_tokens;  // waves past the batch end leave after the IDs
+    const int H = g.num_heads;
+    const int nt = live ? (int)min((int64_t)TW, g.num_tokens - t0) : 0;
+    const int nrows = nt * H;
+    const bool active = lane < nrows;
+    const int my_k = active ? lane / H : 0;
+    const int h = active ? lane - my_k * H : 0;
+    const int64_t t = t0 + my_k;
+
+    int32_t id = 0;
+    if (MODE == kModeHash) {
+        // one round trip: window tokens, query_start_loc and the head records
+        IdInputs in;
+        id_tokens_load(hp, g.tok, g.num_tokens, t, in);
+        QslProbe qp;
+        qsl_probe_load(g.qsl, g.num_reqs, lane, qp);
+        u32x4* lds = head_lds[threadIdx.x >> 6];
+        head_stage_store(hp, hst, H, lane, lds);
+        id_consts_read(hp, lds, h, in);
+        int r;
+        int64_t a;
+        wave_find_request_probed(g.qsl, qp, g.num_reqs, t, t0, nt, my_k, lane, r, a);
+        id = window_id(in, hp.context_len, hp.eos, g.ctx, r, a, t);
+        if (active && g.ids_out != nullptr) g.ids_out[t0 * H + lane] = id;
+    } else {
+        id = active ? g.ids_in[t0 * H + lane] : 0;
+        id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
+    }
+    if (!live) return;  // whole wave
+    // ids mode with rep_of: a repeated row is left for a later copy
+    int skip = 0;
+    if (MODE == kModeIds && g.rep_of != nullptr && active) skip = g.rep_of[t0 * H + lane] != (int32_t)(t0 * H + lane);
+    const float tscale = DTYPE == kFmtNVFP4 ? g.scales[0] : 0.f;
+
+    const StreamArgs sa = stream_args(g, t0, nrows);
+    if (SCALAR_ROWS)
+        stream_rows_scalar<DTYPE, MODE, UNROLL>(g, sa, id, skip, tscale, lane);
+    else
+        stream_rows_lane<DTYPE, MODE, UNROLL>(g, sa, id, skip, tscale, lane);
 }
 
 // IDs only: the lookup kernel's first phase.  Each wave takes 64/H
@@ -236,8 +445,13 @@ __global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int
                                                         const int32_t* __restrict__ qsl, int64_t T, int R,
                                                         const int32_t* __restrict__ ctx,
                                                         int32_t* __restrict__ ids) {
+    __shared__ u32x4 head_lds[4][2 * kWave];
     const int lane = threadIdx.x & (kWave - 1);
+    HeadStage hst;
+    head_stage_load(hp, lane, hst);
+    u32x4* lds = head_lds[threadIdx.x >> 6];
     const int H = hp.num_heads;
+    head_stage_store(hp, hst, H, lane, lds);
     const int TW = kWave / H;
     const int64_t nwaves = (T + TW - 1) / TW;
     for (int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wave < nwaves;
@@ -248,14 +462,15 @@ __global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int
         const int my_k = active ? lane / H : 0;
         const int h = active ? lane - my_k * H : 0;
         const int64_t t = t0 + my_k;
-        int32_t w[PLE_MAX_CONTEXT + 1];
-#pragma unroll
-        for (int j = 0; j <= PLE_MAX_CONTEXT; ++j)
-            w[j] = (j <= hp.context_len) ? tok[t - j >= 0 ? t - j : 0] : 0;
+        IdInputs in;
+        id_tokens_load(hp, tok, T, t, in);
+        id_consts_read(hp, lds, h, in);
+        QslProbe qp;
+        qsl_probe_load(qsl, R, lane, qp);
         int r;
         int64_t a;
-        wave_find_request(qsl, R, t, t0, nt, my_k, lane, r, a);
-        const int32_t id = window_id(hp, w, ctx, r, a, t, h);
+        wave_find_request_probed(qsl, qp, R, t, t0, nt, my_k, lane, r, a);
+        const int32_t id = window_id(in, hp.context_len, hp.eos, ctx, r, a, t);
         if (active) ids[t0 * H + lane] = id;
     }
 }
@@ -306,8 +521,15 @@ static hipError_t launch_lookup_t(const HashParams& hp, const LookupArgs& g, hip
                                              : (DTYPE == kFmtNVFP4 ? PLE_LOOKUP_LOADS_FP4 : PLE_LOOKUP_LOADS_FP8);
     const int64_t waves = (g.num_tokens + g.tokens_per_wave - 1) / g.tokens_per_wave;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK), 0, s, hp,
-                       g);
+    // the scalar-address stream needs rows of 64 x 2^k output chunks
+    const bool scalar_rows = g.cpr_log2 >= 6 && (DTYPE == kFmtBF16 ? PLE_LOOKUP_BF16_SCALAR_ROWS
+                                                                    : PLE_LOOKUP_QUANT_SCALAR_ROWS);
+    if (scalar_rows)
+        hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL, true>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK),
+                           0, s, hp, g);
+    else
+        hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL, false>), dim3((unsigned)blocks),
+                           dim3(PLE_LOOKUP_BLOCK), 0, s, hp, g);
     return hipGetLastError();
 }
 
