@@ -121,6 +121,7 @@ def main() -> int:
               for l in range(L)]
     T, H, D, N = cfg.T, cfg.H, cfg.D, cfg.N
     rows = torch.empty((T, H * D), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty_like(rows) for _ in range(8)]
     kv = torch.empty((T, 2 * N), dtype=torch.bfloat16, device=dev)
     gated = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
@@ -162,23 +163,30 @@ def main() -> int:
     log("timing each kernel")
     reps = max(K, L)
     stage_ms = {
-        "lookup": timed(lambda i: ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=rows), 4 * L),
+        # the lookup writes into 8 rotating output buffers (512 MiB, twice the
+        # last-level cache) so neither its row reads nor its row writes can
+        # stay cached between launches
+        "lookup": timed(lambda i: ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=outs[i % len(outs)]), 4 * L),
         "kv_proj": timed(lambda i: ple.ple_kv_proj(rows, kv_ws[i % 4], kv=kv), reps),
         "gate": timed(lambda i: ple.ple_gate(hidden, kv, eps=cfg.eps, out=gated, want_gate=False), reps),
         "conv": timed(lambda i: ple.ple_conv(gated, qsl, conv_w, dilation=cfg.conv_dilation, y=out), reps),
     }
     lookup_ms = stage_ms["lookup"]
+    # the same launches into one output buffer, as inside the fused step (its
+    # workspace rows are rewritten every layer)
+    lookup_same_ms = timed(lambda i: ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=rows), 4 * L)
     # Reference points for the lookup, same bytes and buffers: the row output
     # written alone (torch fill, no reads), and, for a bf16 table, torch's own
     # embedding gather on the same IDs (an index_select into the same output).
     rows.fill_(1.0)  # first launch loads the kernel: keep it out of the timing
-    write_only_ms = timed(lambda i: rows.fill_(1.0), 4 * L)
+    write_only_ms = timed(lambda i: outs[i % len(outs)].fill_(1.0), 4 * L)
     torch_gather_ms = None
     if fmt == "bf16":
         ids_l = [ple.ple_ngram_ids(hashes[l], toks, qsl).view(-1).long() for l in range(L)]
         rows_flat = rows.view(T * H, D)
         torch.index_select(table, 0, ids_l[0], out=rows_flat)
-        torch_gather_ms = timed(lambda i: torch.index_select(table, 0, ids_l[i % L], out=rows_flat), 4 * L)
+        torch_gather_ms = timed(lambda i: torch.index_select(table, 0, ids_l[i % L],
+                                                            out=outs[i % len(outs)].view(T * H, D)), 4 * L)
         del ids_l
     # streaming-copy ceiling: a device-to-device copy of 1 GiB (four times the
     # last-level cache, so the copy streams from and to HBM)
@@ -231,6 +239,9 @@ def main() -> int:
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
                    "frac_copy_ceiling": round(lookup_gbps / copy_gbps, 4),
                    "tokens_per_s": round(T / (lookup_ms * 1e-3), 1),
+                   "outputs_rotated": 8,
+                   "same_output_ms": round(lookup_same_ms, 5),
+                   "same_output_frac_hbm_peak": round(lookup_bytes / (lookup_same_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                    "write_only_ms": round(write_only_ms, 5),
                    "torch_index_select_ms": None if torch_gather_ms is None else round(torch_gather_ms, 5)},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
