@@ -96,6 +96,54 @@ def test_ids_edge_random(seed):
     np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
 
 
+@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("fmt", ["bf16-32", "bf16-512", "fp8-512", "nvfp4-512"])
+def test_lookup_edge_random(seed, fmt):
+    """The fused lookup on the random edge batches (orders up to 8, head shards of up to 32 heads, empty
+    and one-token requests, frequent EOS, carried context), with vocabularies small enough for a real
+    table: its IDs (ids_out) and rows bit-exact against the oracle.  Rows of 512 elements take the
+    scalar-address row stream for fp8 and NVFP4 (ragged last passes included), the per-lane stream for
+    bf16; 32-element rows the per-lane stream."""
+    rng = np.random.default_rng(5000 + seed)
+    c = _random_case(rng)
+    H, T = c["H"], len(c["toks"])
+    c["V"] = rng.integers(1, 700, size=H).astype(np.int64)
+    c["off"] = np.concatenate([[0], np.cumsum(c["V"])[:-1]]).astype(np.int64)
+    nrows = int(c["V"].sum())
+    R = len(c["qsl"]) - 1
+    log(f"lookup edge {fmt} seed={seed} T={T} R={R} C={c['C']} H={H} first={c['first']}")
+    want_ids = oracle.ngram_ids(c["toks"], c["qsl"], c["mult"], c["V"], c["off"], context_len=c["C"],
+                                heads_per_ngram=c["hpn"], eos_token_id=c["eos"], ngram_context=c["ctx"],
+                                first_head=c["first"])
+    kind, D = fmt.split("-")[0], int(fmt.split("-")[1])
+    if kind == "bf16":
+        table = rng.integers(0, 65536, size=(nrows, D), dtype=np.uint16)
+        tb, keep = ple.Table.from_tensor(dev_bf16(table)), None
+        want = table[want_ids.reshape(-1)] if T else np.zeros((0, D), np.uint16)
+    elif kind == "fp8":
+        codes = rng.integers(0, 256, size=(nrows, D), dtype=np.uint8)
+        scales = np.exp(rng.uniform(-8, 8, nrows)).astype(np.float32)
+        keep = (dev(codes), dev(scales))
+        tb = ple.Table.from_tensor(*keep)
+        want = oracle.gather_fp8(codes, scales, want_ids)
+    else:
+        codes = rng.integers(0, 256, size=(nrows, D // 2), dtype=np.uint8)
+        bsc = rng.integers(0, 256, size=(nrows, D // 16), dtype=np.uint8)
+        tsc = np.asarray([0.37], np.float32)
+        keep = (dev(codes), dev(bsc), dev(tsc))
+        tb = ple.Table.nvfp4(*keep)
+        want = oracle.gather_nvfp4(codes, bsc, tsc[0], want_ids)
+    hp = ple.HashParams(c["mult"], c["V"], c["off"], heads_per_ngram=c["hpn"], context_len=c["C"],
+                        eos_token_id=c["eos"], first_head=c["first"])
+    toks = dev(c["toks"]) if T else torch.zeros(0, dtype=torch.int32, device=DEV)
+    ids_out = torch.full((T, H), -1, dtype=torch.int32, device=DEV)
+    rows = ple.ple_lookup(hp, tb, toks, dev(c["qsl"]), ngram_context=None if c["ctx"] is None else dev(c["ctx"]),
+                          ids_out=ids_out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids_out.cpu().numpy(), want_ids)
+    np.testing.assert_array_equal(host_bits(rows).reshape(-1, D), want.reshape(-1, D))
+
+
 def test_ids_golden_cases():
     cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hash_cases.json")))["cases"]
     for c in cases:
