@@ -163,6 +163,10 @@ def main() -> int:
     # as inside the fused step, each launched back to back
     log("timing each kernel")
     reps = max(K, L)
+    # Every timed kernel reads real data: rows from a lookup here, kv and gated
+    # from the loops before theirs.  (The matrix cores run measurably faster on
+    # zero operands: kv_proj on a zero-filled x takes ~10% less time.)
+    ple.ple_lookup(hashes[0], tb, toks, qsl, rows=rows)
     stage_ms = {
         # the lookup writes into 8 rotating output buffers (512 MiB, twice the
         # last-level cache) so neither its row reads nor its row writes can
