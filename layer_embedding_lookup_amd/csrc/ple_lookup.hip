@@ -10,14 +10,16 @@
 //
 // Design for CDNA4: each wave owns a few consecutive tokens (at most 64
 // (token, head) rows).  One lane per row computes the ID in registers: the
-// wave finds request boundaries with one cooperative load of query_start_loc
-// and ballots, the window tokens are loaded in the same round trip, and the
-// modulo is a Barrett reduction instead of a 64-bit divide.  The IDs never
-// leave registers: the wave then streams its rows with 16-byte loads (one wave
-// instruction moves a whole 1 KiB bf16 row; the row's ID comes from the
-// owning lane by a cross-lane read), 16 loads in flight per lane, and writes
-// coalesced 16-byte chunks into the wave's contiguous [tokens][H*D] slab.
-// Waves never wait for each other.
+// per-head hash constants come from the kernel arguments through a per-wave
+// LDS stage filled by one load at entry, the wave finds request boundaries
+// with one cooperative load of query_start_loc and ballots, the window tokens
+// are loaded in the same round trip, and the modulo is a Barrett reduction
+// instead of a 64-bit divide.  The IDs never leave registers: the wave then
+// streams its rows with 16-byte loads (one wave instruction moves a whole
+// 1 KiB bf16 row), 16 loads in flight per lane, and writes coalesced 16-byte
+// chunks into the wave's contiguous [tokens][H*D] slab, either with per-lane
+// addresses (row IDs by cross-lane reads) or, for rows of 64 x 2^k chunks,
+// from scalar row bases with buffer stores.  Waves never wait for each other.
 #include "ple_launch.h"
 
 // Tuning knobs (compile-time): 16-byte output chunks per lane per pass by
