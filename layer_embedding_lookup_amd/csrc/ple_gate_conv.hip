@@ -20,6 +20,10 @@
 #define PLE_CONV_TOKENS_PER_BLOCK 32
 #endif
 
+#ifndef PLE_CONV_CPL
+#define PLE_CONV_CPL 2  // conv_rows_kernel: 16-byte chunks per lane per pass (2 beat 1, 4 and 8 on gfx950)
+#endif
+
 namespace ple {
 
 constexpr int kConvKMax = 8;  // kernel sizes above this use the generic kernel
@@ -388,12 +392,6 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     const int lane = tid & (kWave - 1);
     const int wv = tid >> 6;
     const int nch = N >> 3;
-    for (int i = tid; i < nch * KC; i += 256) {
-        const int c = i / KC, q = i - (i / KC) * KC;
-        s_wv[q * nch + c] = ((const u32x4*)w)[i];
-    }
-    __syncthreads();
-
     const int64_t S = (int64_t)(KC - 1) * d;
     const int xcd = blockIdx.x & 7;
     const int64_t blocks_per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
@@ -401,11 +399,36 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     const int64_t t_begin = xcd * per_xcd;
     const int64_t t_end = min(T, t_begin + per_xcd);
     const int64_t stride = blocks_per_xcd * 4;
-    constexpr int CPL = 2;  // 16-byte chunks per lane per pass (2 beat 1, 4 and 8 on gfx950)
+    const int64_t t_first = t_begin + (int64_t)(blockIdx.x >> 3) * 4 + wv;
+    constexpr int CPL = PLE_CONV_CPL;  // 16-byte chunks per lane per pass
 
-    for (int64_t t = t_begin + (int64_t)(blockIdx.x >> 3) * 4 + wv; t < t_end; t += stride) {
+    // the first token's query_start_loc probe goes out with the weight
+    // staging, so that its round trip overlaps the staging's
+    QslProbe qp;
+    qsl_probe_load(qsl, R, lane, qp);
+    for (int i = tid; i < nch * KC; i += 256) {
+        const int c = i / KC, q = i - (i / KC) * KC;
+        s_wv[q * nch + c] = ((const u32x4*)w)[i];
+    }
+    __syncthreads();
+
+    for (int64_t t = t_first; t < t_end; t += stride) {
         int r = 0;
         int64_t a = 0;
+        if (t == t_first)
+            wave_find_request_probed(qsl, qp, R, t, t, 1, 0, lane, r, a);
+        else
+            wave_find_request(qsl, R, t, t, 1, 0, lane, r, a);
+        // tap i of this token: the batch row t - i*d within the request, else
+        // the carried state row (oldest first), else zero; resolved before any
+        // load, so each pass is one round trip
+        const uint16_t* src[KC];
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int64_t p = t - (int64_t)i * d;
+            src[i] = p >= a ? x + p * N
+                            : (state != nullptr ? state + ((int64_t)r * S + (S - (a - p))) * N : nullptr);
+        }
         for (int cb = 0; cb < nch; cb += kWave * CPL) {
             u32x4 xv[CPL][KC];
 #pragma unroll
@@ -413,25 +436,9 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
                 const int c = cb + j * kWave + lane;
 #pragma unroll
                 for (int i = 0; i < KC; ++i) {
-                    const int64_t p = t - (int64_t)i * d;
                     u32x4 v = {0u, 0u, 0u, 0u};
-                    if (c < nch && p >= 0) v = *(const u32x4*)(x + p * N + (int64_t)c * 8);
+                    if (c < nch && src[i] != nullptr) v = *(const u32x4*)(src[i] + (int64_t)c * 8);
                     xv[j][i] = v;
-                }
-            }
-            if (cb == 0) wave_find_request(qsl, R, t, t, 1, 0, lane, r, a);  // wave-uniform branch
-#pragma unroll
-            for (int i = 1; i < KC; ++i) {
-                const int64_t p = t - (int64_t)i * d;
-                if (p < a) {  // wave-uniform: before this request's first token
-#pragma unroll
-                    for (int j = 0; j < CPL; ++j) {
-                        const int c = cb + j * kWave + lane;
-                        u32x4 v = {0u, 0u, 0u, 0u};
-                        if (state != nullptr && c < nch)
-                            v = *(const u32x4*)(state + ((int64_t)r * S + (S - (a - p))) * N + (int64_t)c * 8);
-                        xv[j][i] = v;
-                    }
                 }
             }
 #pragma unroll
