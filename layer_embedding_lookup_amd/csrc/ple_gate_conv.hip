@@ -21,7 +21,7 @@
 #endif
 
 #ifndef PLE_CONV_CPL
-#define PLE_CONV_CPL 2  // conv_rows_kernel: 16-byte chunks per lane per pass (2 beat 1, 4 and 8 on gfx950)
+#define PLE_CONV_CPL 2  // conv_rows_kernel, rows wider than 256 chunks: 16-byte chunks per lane per pass (2 beat 1, 4 and 8 at 4096 channels)
 #endif
 
 namespace ple {
@@ -54,6 +54,10 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
     const u32x4* __restrict__ v = k + nch;
     u32x4* __restrict__ o = (u32x4*)(out + t * N);
 
+    // a row of at most 64 x UNROLL chunks is one pass: its value half is
+    // loaded with h and k, so the wave makes one round trip, not two
+    const bool one_pass = nch <= 64 * UNROLL;
+    u32x4 vpre[UNROLL];
     float hh = 0.f, kk = 0.f, hk = 0.f;
     for (int base = lane; base < nch; base += 64 * UNROLL) {
         u32x4 hv[UNROLL], kv4[UNROLL];
@@ -63,6 +67,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
             if (idx < nch) {
                 hv[u] = h[idx];
                 kv4[u] = k[idx];
+                if (one_pass) vpre[u] = v[idx];
             }
         }
 #pragma unroll
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
         u32x4 vv[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            if (base + 64 * u < nch) vv[u] = v[base + 64 * u];
+            if (base + 64 * u < nch) vv[u] = one_pass ? vpre[u] : v[base + 64 * u];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + 64 * u;
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(256) void conv_lds_kernel(const uint16_t* __restric
 // speculatively together with the request lookup (one round trip); taps that
 // fall before the request start are then replaced by the carried state (or
 // zero).
-template <int KC>
+template <int KC, int CPL>
 __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restrict__ x,
                                                         const int32_t* __restrict__ qsl, int64_t T, int R,
                                                         const uint16_t* __restrict__ state,
@@ -400,7 +405,6 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     const int64_t t_end = min(T, t_begin + per_xcd);
     const int64_t stride = blocks_per_xcd * 4;
     const int64_t t_first = t_begin + (int64_t)(blockIdx.x >> 3) * 4 + wv;
-    constexpr int CPL = PLE_CONV_CPL;  // 16-byte chunks per lane per pass
 
     // the first token's query_start_loc probe goes out with the weight
     // staging, so that its round trip overlaps the staging's
@@ -472,11 +476,11 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     }
 }
 
-template <int KC>
-static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
-                                   const uint16_t* w, int N, int d, uint16_t* y, hipStream_t s) {
+template <int KC, int CPL>
+static hipError_t launch_conv_rows_t(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
+                                     const uint16_t* w, int N, int d, uint16_t* y, hipStream_t s) {
     const size_t lds = (size_t)N * KC * 2;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)conv_rows_kernel<KC>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)conv_rows_kernel<KC, CPL>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (attr != hipSuccess) return attr;
     // resident blocks per device for this kernel and weight size (queried once)
@@ -491,7 +495,8 @@ static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_
         if (it == resident.end()) {
             int cus = 256, per_cu = 1;
             (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC>, 256, lds) != hipSuccess ||
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC, CPL>, 256, lds) !=
+                    hipSuccess ||
                 per_cu < 1)
                 per_cu = 1;
             it = resident.emplace(std::make_pair(dev, lds), (int64_t)cus * per_cu).first;
@@ -501,9 +506,19 @@ static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_
     const int64_t need = (T + 3) / 4;                        // one wave per token at most
     if (blocks > need) blocks = need;
     blocks = ((blocks + 7) / 8) * 8;                         // whole XCD rounds
-    hipLaunchKernelGGL((conv_rows_kernel<KC>), dim3((unsigned)blocks), dim3(256), lds, s, x, qsl, T, R, state, w, N,
-                       d, y);
+    hipLaunchKernelGGL((conv_rows_kernel<KC, CPL>), dim3((unsigned)blocks), dim3(256), lds, s, x, qsl, T, R, state, w,
+                       N, d, y);
     return hipGetLastError();
+}
+
+// Rows of at most 256 16-byte chunks (N <= 2048) go in one pass of 4 chunks
+// per lane, so a token costs one round trip; wider rows take passes of 2
+// (measured best for the 4096-wide prefill).
+template <int KC>
+static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
+                                   const uint16_t* w, int N, int d, uint16_t* y, hipStream_t s) {
+    if ((N >> 3) <= 4 * kWave) return launch_conv_rows_t<KC, 4>(x, qsl, T, R, state, w, N, d, y, s);
+    return launch_conv_rows_t<KC, PLE_CONV_CPL>(x, qsl, T, R, state, w, N, d, y, s);
 }
 
 // state_out[r][m] = the (S-m)-th most recent conv input of state[r] ++ x[a:b].
