@@ -512,10 +512,12 @@ def bench_decode(args):
     out = torch.empty((T, cfg.N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def step(s, swap=True):
+    def step(s, swap=True, hint=1):
+        # one token per request: the fused entry point's one-kernel decode tail
         l = s % L
         ple.ple_prefill_fused(layers[l], toks, qsl, hidden, ngram_context=ctx[l][0], ngram_context_out=ctx[l][1],
-                              conv_state=st[l][0], conv_state_out=st[l][1], out=out, workspace=ws)
+                              conv_state=st[l][0], conv_state_out=st[l][1], out=out, workspace=ws,
+                              max_request_tokens=hint)
         if swap:
             st[l].reverse()
             ctx[l].reverse()
@@ -529,6 +531,15 @@ def bench_decode(args):
         step(s)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    # the same steps without the hint (separate gate, conv and state kernels)
+    for s in range(L):
+        step(s, hint=0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s, hint=0)
+    torch.cuda.synchronize()
+    unhinted_ms = (time.perf_counter() - t0) * 1e3 / K
     graphs = []
     for l in range(L):
         g = torch.cuda.CUDAGraph()
@@ -557,6 +568,7 @@ def bench_decode(args):
                        "dim": D, "hidden": N, "kv_proj": [H * D, 2 * N], "conv": [cfg.conv_kernel, cfg.conv_dilation],
                        "context_len": cfg.context_len, "layers_rotated": L},
             "graph_ms_per_step": round(ms_per_step, 4),
+            "separate_kernels_ms_per_step": round(unhinted_ms, 4),
             "step_bytes": step_bytes,
             "step_GBps": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)}
     print(json.dumps(line), flush=True)

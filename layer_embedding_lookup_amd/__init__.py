@@ -137,11 +137,11 @@ class Layer:
 
 
 def _batch(input_ids, query_start_loc, ngram_context=None, ngram_context_out=None, conv_state=None,
-           conv_state_out=None, num_tokens=None) -> capi.ple_batch_desc:
+           conv_state_out=None, num_tokens=None, max_request_tokens=0) -> capi.ple_batch_desc:
     T = int(input_ids.shape[0]) if input_ids is not None else int(num_tokens)
     R = int(query_start_loc.shape[0]) - 1
-    return capi.ple_batch_desc(_ptr(input_ids), _ptr(query_start_loc), T, R, 0, _ptr(ngram_context),
-                               _ptr(ngram_context_out), _ptr(conv_state), _ptr(conv_state_out))
+    return capi.ple_batch_desc(_ptr(input_ids), _ptr(query_start_loc), T, R, int(max_request_tokens),
+                               _ptr(ngram_context), _ptr(ngram_context_out), _ptr(conv_state), _ptr(conv_state_out))
 
 
 def _device_of(t: torch.Tensor) -> torch.device:
@@ -297,7 +297,9 @@ def prefill_conv_input(layer: Layer, workspace, num_tokens: int):
 
 def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefetched_rows=None, ngram_context=None,
                       ngram_context_out=None, conv_state=None, conv_state_out=None, out=None, gate=None,
-                      workspace=None, stream=None):
+                      workspace=None, max_request_tokens=0, stream=None):
+    """max_request_tokens: 0 (unknown) or 1 (no request has more than one token: a decode batch,
+    run with one kernel for gate, conv and the carried state and context)."""
     T, N = hidden.shape
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=hidden.device)
@@ -305,7 +307,8 @@ def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefe
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=hidden.device)
     L = layer.desc()
-    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out)
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out,
+               max_request_tokens=max_request_tokens)
     capi.check(capi.load().ple_prefill_fused(ctypes.byref(L), ctypes.byref(b), _ptr(hidden), _ptr(prefetched_rows),
                                              _ptr(out), _ptr(gate), _ptr(workspace), workspace.numel(),
                                              _stream(stream)), "ple_prefill_fused")

@@ -45,7 +45,7 @@ class ple_table_desc(ctypes.Structure):
 
 class ple_batch_desc(ctypes.Structure):
     _fields_ = [("input_ids", P), ("query_start_loc", P), ("num_tokens", I64), ("num_reqs", I32),
-                ("reserved", I32), ("ngram_context", P), ("ngram_context_out", P),
+                ("max_request_tokens", I32), ("ngram_context", P), ("ngram_context_out", P),
                 ("conv_state", P), ("conv_state_out", P)]
 
 

@@ -159,6 +159,7 @@ int validate_batch_tokens(const ple_batch_desc* b) {
     if (b->num_reqs < 0) return fail(PLE_ERR_INVALID_ARGUMENT, "num_reqs < 0");
     if (b->num_reqs == 0 && b->num_tokens > 0)
         return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens > 0 with num_reqs == 0");
+    if (b->max_request_tokens < 0) return fail(PLE_ERR_INVALID_ARGUMENT, "max_request_tokens < 0");
     if (b->num_reqs > 0 && (b->query_start_loc == nullptr || !aligned4(b->query_start_loc)))
         return fail(PLE_ERR_INVALID_ARGUMENT, "query_start_loc is NULL or misaligned");
     if (b->num_tokens > 0 && (b->input_ids == nullptr || !aligned4(b->input_ids)))
@@ -659,6 +660,35 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
         }
         e = launch_kv_proj(x, layer->kv_weight, T, HD, 2 * N, kv, s);
         if (e != hipSuccess) return hip_fail(e, "kv_proj launch");
+    }
+    // decode batches (at most one token per request): gate, conv and the
+    // carried state and context in one launch
+    if (batch->max_request_tokens == 1 && decode_tail_supported(layer->conv_kernel)) {
+        DecodeTailArgs a;
+        a.hidden = hidden;
+        a.kv = kv;
+        a.qsl = batch->query_start_loc;
+        a.tok = batch->input_ids;
+        a.T = T;
+        a.R = batch->num_reqs;
+        a.N = N;
+        a.eps = layer->eps;
+        a.d = layer->conv_dilation;
+        a.conv_w = layer->conv_weight;
+        a.state = batch->conv_state;
+        a.state_out = state_work ? batch->conv_state_out : nullptr;
+        a.ctx = batch->ngram_context;
+        a.ctx_out = ctx_work ? batch->ngram_context_out : nullptr;
+        a.C = ctx_work ? layer->hash.context_len : 0;
+        a.eos = layer->hash.eos_token_id;
+        a.gated = gated;
+        a.y = out;
+        a.gate = gate;
+        e = launch_decode_tail(a, layer->conv_kernel, s);
+        if (e != hipSuccess) return hip_fail(e, "decode tail launch");
+        return ok();
+    }
+    if (T > 0) {
         e = launch_gate(hidden, kv, T, N, layer->eps, gated, gate, s);
         if (e != hipSuccess) return hip_fail(e, "gate launch");
     }

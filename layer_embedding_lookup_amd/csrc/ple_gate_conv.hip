@@ -41,6 +41,28 @@ __device__ __forceinline__ void acc_dot(u32x4 a, u32x4 b, float& aa, float& bb, 
     }
 }
 
+// The gate of one token from the wave's per-lane fp32 partial sums of h.h,
+// k.k and h.k: reduced across the wave in double, then
+// g = sigmoid(<h, k> / (rms(h) rms(k) sqrt(N))) with eps inside each root.
+__device__ __forceinline__ float token_gate(float hh, float kk, float hk, int N, float eps) {
+    double dhh = hh, dkk = kk, dhk = hk;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        dhh += __shfl_xor(dhh, off, 64);
+        dkk += __shfl_xor(dkk, off, 64);
+        dhk += __shfl_xor(dhk, off, 64);
+    }
+    const double n = (double)N;
+    const double s = dhk / (sqrt(dhh / n + (double)eps) * sqrt(dkk / n + (double)eps) * sqrt(n));
+    return (float)(1.0 / (1.0 + exp(-s)));
+}
+
+// 8 gated values g * v, rounded to bf16
+__device__ __forceinline__ u32x4 gate_chunk(float g, u32x4 x) {
+    return u32x4{pack_bf16x2(g * bf16_lo(x.x), g * bf16_hi(x.x)), pack_bf16x2(g * bf16_lo(x.y), g * bf16_hi(x.y)),
+                 pack_bf16x2(g * bf16_lo(x.z), g * bf16_hi(x.z)), pack_bf16x2(g * bf16_lo(x.w), g * bf16_hi(x.w))};
+}
+
 template <int UNROLL>
 __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ hidden,
                                                    const uint16_t* __restrict__ kv, int64_t T, int N, float eps,
@@ -74,16 +96,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
         for (int u = 0; u < UNROLL; ++u)
             if (base + 64 * u < nch) acc_dot(hv[u], kv4[u], hh, kk, hk);
     }
-    double dhh = hh, dkk = kk, dhk = hk;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        dhh += __shfl_xor(dhh, off, 64);
-        dkk += __shfl_xor(dkk, off, 64);
-        dhk += __shfl_xor(dhk, off, 64);
-    }
-    const double n = (double)N;
-    const double s = dhk / (sqrt(dhh / n + (double)eps) * sqrt(dkk / n + (double)eps) * sqrt(n));
-    const float g = (float)(1.0 / (1.0 + exp(-s)));
+    const float g = token_gate(hh, kk, hk, N, eps);
     if (lane == 0 && gate != nullptr) gate[t] = g;
 
     for (int base = lane; base < nch; base += 64 * UNROLL) {
@@ -94,13 +107,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + 64 * u;
-            if (idx < nch) {
-                const u32x4 x = vv[u];
-                o[idx] = u32x4{pack_bf16x2(g * bf16_lo(x.x), g * bf16_hi(x.x)),
-                               pack_bf16x2(g * bf16_lo(x.y), g * bf16_hi(x.y)),
-                               pack_bf16x2(g * bf16_lo(x.z), g * bf16_hi(x.z)),
-                               pack_bf16x2(g * bf16_lo(x.w), g * bf16_hi(x.w))};
-            }
+            if (idx < nch) o[idx] = gate_chunk(g, vv[u]);
         }
     }
 }
@@ -113,6 +120,33 @@ __device__ __forceinline__ void unpack8(u32x4 x, float f[8]) {
 }
 
 __device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+
+// One 16-byte output chunk (8 channels) of the convolution: wq[q] holds the
+// 8 x KC weights of the chunk's channels (channel-major, [8][KC] bf16) as KC
+// 16-byte chunks, xv[i] the 8 inputs of tap i (token t - i*d; tap i meets
+// weight KC-1-i).  fp32 accumulation from the current token back, bf16 out.
+template <int KC>
+__device__ __forceinline__ u32x4 conv_chunk(const u32x4 (&wq)[KC], const u32x4 (&xv)[KC]) {
+    uint32_t wd[4 * KC];
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+        wd[4 * q] = wq[q].x; wd[4 * q + 1] = wq[q].y; wd[4 * q + 2] = wq[q].z; wd[4 * q + 3] = wq[q].w;
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        float f[8];
+        unpack8(xv[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int flat = e * KC + (KC - 1 - i);  // w[c*8+e][KC-1-i]
+            const float wt = (flat & 1) ? bf16_hi(wd[flat >> 1]) : bf16_lo(wd[flat >> 1]);
+            acc[e] += wt * f[e];
+        }
+    }
+    return u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                 pack_bf16x2(acc[6], acc[7])};
+}
 
 // One lane per (token, 8 channels).  KC > 0: compile-time kernel size with the
 // 8 x KC weights read as KC 16-byte chunks; KC == 0: any kernel size, scalar
@@ -449,27 +483,10 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
             for (int j = 0; j < CPL; ++j) {
                 const int c = cb + j * kWave + lane;
                 if (c < nch) {
-                    uint32_t wd[4 * KC];
+                    u32x4 wq[KC];
 #pragma unroll
-                    for (int q = 0; q < KC; ++q) {
-                        const u32x4 v4 = s_wv[q * nch + c];
-                        wd[4 * q] = v4.x; wd[4 * q + 1] = v4.y; wd[4 * q + 2] = v4.z; wd[4 * q + 3] = v4.w;
-                    }
-                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int i = 0; i < KC; ++i) {
-                        float f[8];
-                        unpack8(xv[j][i], f);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int flat = e * KC + (KC - 1 - i);  // w[c*8+e][KC-1-i]
-                            const float wt = (flat & 1) ? bf16_hi(wd[flat >> 1]) : bf16_lo(wd[flat >> 1]);
-                            acc[e] += wt * f[e];
-                        }
-                    }
-                    *(u32x4*)(y + t * N + (int64_t)c * 8) =
-                        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                              pack_bf16x2(acc[6], acc[7])};
+                    for (int q = 0; q < KC; ++q) wq[q] = s_wv[q * nch + c];
+                    *(u32x4*)(y + t * N + (int64_t)c * 8) = conv_chunk<KC>(wq, xv[j]);
                 }
             }
         }
@@ -536,6 +553,125 @@ __global__ __launch_bounds__(256) void conv_state_out_kernel(const uint16_t* __r
         int64_t a, b;
         carried_window(qsl, T, r, nullptr, a, b);
         carry_state_row(x, state, N, S, r, m, a, b, state_out, lane);
+    }
+}
+
+// Decode tail: gate, conv and the carried state and context of a batch in
+// which every request has at most one token, in one launch.  Two waves per
+// request.  The first takes the request's token t (if any): its gate from
+// the h and k rows, the gated row g*v (written to `gated`, the conv input),
+// the conv output, whose older taps all lie before the request start and so
+// come from the carried state (or are zero), and the newest carried state
+// row (the gated row).  The second shifts the carried state by the request's
+// token count (rows 1.. of the old state; all of it for an empty request) and
+// writes the carried context.  The conv's weights, taps and value rows are
+// loaded with the h and k rows, so the token costs one round trip after the
+// request lookup.  Arithmetic is that of gate_kernel and conv_rows_kernel
+// (token_gate, gate_chunk, conv_chunk), so the results are the same bits.
+// Requests with more than one token are left unwritten (the caller promised
+// none); every access stays in bounds for any query_start_loc.
+template <int KC>
+__global__ __launch_bounds__(256) void decode_tail_kernel(DecodeTailArgs a) {
+    constexpr int G = 4;  // 16-byte chunks per lane per pass
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r = blockIdx.x * 2 + (wid >> 1);
+    if (r >= a.R) return;  // whole wave
+    int64_t ta, tb;
+    carried_window(a.qsl, a.T, r, nullptr, ta, tb);
+    const int64_t n = tb - ta;
+    const int N = a.N, nch = N >> 3;
+    const int S = (KC - 1) * a.d;
+
+    if ((wid & 1) == 1) {  // carried state shift and context
+        if (a.state_out != nullptr && S > 0 && n <= 1)
+            for (int m = 0; m < S - (int)n; ++m) carry_state_row(a.gated, a.state, N, S, r, m, ta, tb, a.state_out, lane);
+        if (a.ctx_out != nullptr && lane < a.C)
+            a.ctx_out[(int64_t)r * a.C + lane] = carried_token(a.tok, a.ctx, a.C, a.eos, r, lane, ta, tb);
+        return;
+    }
+    if (n != 1) return;
+    const int64_t t = ta;
+    const u32x4* __restrict__ h = (const u32x4*)(a.hidden + t * N);
+    const u32x4* __restrict__ k = (const u32x4*)(a.kv + t * 2 * (int64_t)N);
+    const u32x4* __restrict__ v = k + nch;
+    const u32x4* __restrict__ wc = (const u32x4*)a.conv_w;  // chunk c's weights: KC chunks from c*KC
+    // older tap i (1..KC-1) of chunk c: carried state row S - i*d of request r, or zero
+    auto tap_row = [&](int i) -> const u32x4* {
+        return a.state != nullptr ? (const u32x4*)(a.state + ((int64_t)r * S + (S - i * a.d)) * N) : nullptr;
+    };
+    auto load_pass = [&](int c0, u32x4 (&vv)[G], u32x4 (&xv)[G][KC], u32x4 (&wq)[G][KC]) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int c = c0 + j * kWave + lane;
+            const bool in = c < nch;
+            vv[j] = in ? v[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 1; i < KC; ++i) {
+                const u32x4* tr = tap_row(i);
+                xv[j][i] = (in && tr != nullptr) ? tr[c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int q = 0; q < KC; ++q) wq[j][q] = in ? wc[(int64_t)c * KC + q] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    u32x4 vv[G], xv[G][KC], wq[G][KC];
+    load_pass(0, vv, xv, wq);  // independent of the gate: in flight with h and k
+
+    // per-lane partial sums in gate_kernel's order (chunks lane, lane+64, ...)
+    constexpr int UNROLL = 8;
+    float hh = 0.f, kk = 0.f, hk = 0.f;
+    for (int base = lane; base < nch; base += 64 * UNROLL) {
+        u32x4 hv[UNROLL], kv4[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int idx = base + 64 * u;
+            if (idx < nch) {
+                hv[u] = h[idx];
+                kv4[u] = k[idx];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            if (base + 64 * u < nch) acc_dot(hv[u], kv4[u], hh, kk, hk);
+    }
+    const float g = token_gate(hh, kk, hk, N, a.eps);
+    if (lane == 0 && a.gate != nullptr) a.gate[t] = g;
+
+    for (int c0 = 0; c0 < nch; c0 += G * kWave) {
+        if (c0 > 0) load_pass(c0, vv, xv, wq);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int c = c0 + j * kWave + lane;
+            if (c < nch) {
+                const u32x4 gv = gate_chunk(g, vv[j]);
+                xv[j][0] = gv;
+                ((u32x4*)(a.gated + t * N))[c] = gv;
+                if (a.state_out != nullptr && S > 0)
+                    ((u32x4*)(a.state_out + ((int64_t)r * S + (S - 1)) * N))[c] = gv;
+                ((u32x4*)(a.y + t * N))[c] = conv_chunk<KC>(wq[j], xv[j]);
+            }
+        }
+    }
+}
+
+template <int KC>
+static hipError_t launch_decode_tail_t(const DecodeTailArgs& a, hipStream_t s) {
+    const int64_t blocks = ((int64_t)a.R + 1) / 2;  // two requests (four waves) per block
+    hipLaunchKernelGGL(decode_tail_kernel<KC>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+bool decode_tail_supported(int K) { return K >= 1 && K <= 4; }
+
+hipError_t launch_decode_tail(const DecodeTailArgs& a, int K, hipStream_t s) {
+    if (a.R <= 0) return hipSuccess;
+    switch (K) {
+        case 1: return launch_decode_tail_t<1>(a, s);
+        case 2: return launch_decode_tail_t<2>(a, s);
+        case 3: return launch_decode_tail_t<3>(a, s);
+        case 4: return launch_decode_tail_t<4>(a, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -48,6 +48,32 @@ hipError_t launch_select_rows(const uint16_t* gathered, int E, int64_t slot, int
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s);
 
+// Gate, conv and carried state/context for batches of at most one token per
+// request (decode), one launch; K = conv kernel size (decode_tail_supported).
+struct DecodeTailArgs {
+    const uint16_t* hidden;  // [T][N]
+    const uint16_t* kv;      // [T][2N]
+    const int32_t* qsl;      // [R+1]
+    const int32_t* tok;      // [T]
+    int64_t T;
+    int32_t R;
+    int32_t N;
+    float eps;
+    int32_t d;               // conv dilation
+    const uint16_t* conv_w;  // [N][K]
+    const uint16_t* state;   // [R][S][N] or NULL
+    uint16_t* state_out;     // [R][S][N] or NULL
+    const int32_t* ctx;      // [R][C] or NULL
+    int32_t* ctx_out;        // [R][C] or NULL
+    int32_t C;
+    int32_t eos;
+    uint16_t* gated;         // [T][N], the conv input
+    uint16_t* y;             // [T][N]
+    float* gate;             // [T] or NULL
+};
+bool decode_tail_supported(int K);
+hipError_t launch_decode_tail(const DecodeTailArgs& a, int K, hipStream_t s);
+
 hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, uint16_t* out,
                        float* gate, hipStream_t s);
 hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,

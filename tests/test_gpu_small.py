@@ -469,6 +469,64 @@ def test_prefill_fused_parity_small(variant):
     assert np.abs(bf16_f64(host_bits(st_out)) - bf16_f64(st_ref)).max() <= GATE_ABS_TOL
 
 
+def _run_fused_both(cfg, b, L, hidden, *, with_ctx, with_state, max_request_tokens, T=None):
+    """One ple_prefill_fused call; returns out, gate, conv input, state out and context out (host)."""
+    T = cfg.T if T is None else T
+    S = (L.conv_weight.shape[1] - 1) * L.conv_dilation
+    st_out = torch.full((b.R, S, cfg.N), 7.0, dtype=torch.bfloat16, device=DEV)
+    ctx_out = torch.full((b.R, cfg.context_len), -3, dtype=torch.int32, device=DEV)
+    gate = torch.full((T,), -1.0, dtype=torch.float32, device=DEV)
+    ws = torch.zeros((ple.ple_prefill_workspace_bytes(L, T),), dtype=torch.uint8, device=DEV)
+    toks = dev(b.input_ids) if T else torch.zeros(0, dtype=torch.int32, device=DEV)
+    out = ple.ple_prefill_fused(L, toks, dev(b.qsl), dev_bf16(hidden),
+                                ngram_context=dev(b.ngram_context) if with_ctx else None, ngram_context_out=ctx_out,
+                                conv_state=dev_bf16(b.conv_state) if with_state else None, conv_state_out=st_out,
+                                gate=gate, workspace=ws, max_request_tokens=max_request_tokens)
+    torch.cuda.synchronize()
+    return (host_bits(out), gate.cpu().numpy(), host_bits(ple.prefill_conv_input(L, ws, T)), host_bits(st_out),
+            ctx_out.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["decode-256", "decode-256-fresh", "tiny-empty-requests-k4", "tiny-k1", "tiny-k2",
+                                  "tiny-k3-fresh", "all-empty"])
+def test_decode_tail_equals_plain_path(case):
+    """With max_request_tokens = 1 the fused entry point runs gate, conv and the carried state and
+    context as one kernel; every output is the same bits as the separate kernels' (same arithmetic),
+    including the conv input left in the workspace, on batches of one-token and empty requests."""
+    import dataclasses
+    if case.startswith("decode-256"):
+        cfg = wl.CONFIGS[2]
+        b = wl.make_batch(cfg, with_context=True, with_state=True)
+        K = cfg.conv_kernel
+    else:
+        base = wl.CONFIGS[1]
+        K = {"tiny-empty-requests-k4": 4, "tiny-k1": 1, "tiny-k2": 2, "tiny-k3-fresh": 3, "all-empty": 4}[case]
+        lens = [0, 0, 0] if case == "all-empty" else [1, 0, 1, 1, 0, 0, 1, 1, 0, 1]
+        cfg = dataclasses.replace(base, idx=60, T=int(sum(lens)), conv_kernel=K)
+        b = wl.make_batch(base, with_context=True, with_state=True)
+        rng = np.random.default_rng(61 + K)
+        R = len(lens)
+        qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        S = (K - 1) * cfg.conv_dilation
+        b = dataclasses.replace(b, cfg=cfg, input_ids=rng.integers(0, 1000, size=cfg.T).astype(np.int32), qsl=qsl,
+                                ngram_context=rng.integers(0, 1000, size=(R, cfg.context_len)).astype(np.int32),
+                                conv_state=wl.normal_bf16((R, S, cfg.N), 62, 0.125))
+    fresh = case.endswith("fresh")
+    table, scales, tb, keep = _table_dev(cfg)
+    kvw = wl.make_kv_weight(cfg)
+    cw = wl.normal_bf16((cfg.N, K), 63 + K, 0.3)
+    L = ple.Layer(hash_params(b), tb, dev_bf16(kvw), dev_bf16(cw), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    hidden = wl.make_hidden(cfg, T=max(cfg.T, 1))[:cfg.T]
+    log(f"decode tail {case}: T={cfg.T} R={b.R} K={K}")
+    plain = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=0)
+    tail = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=1)
+    for name, x, y in zip(["out", "gate", "conv input", "state out", "context out"], plain, tail):
+        np.testing.assert_array_equal(y, x, err_msg=name)
+    if case == "decode-256":  # and against the oracle
+        ref = _oracle_chain(cfg, b, table, scales, kvw, cw, hidden)
+        assert np.abs(bf16_f64(tail[0]) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
+
+
 def test_prefill_with_prefetched_rows_equals_plain():
     cfg = wl.CONFIGS[2]
     b = wl.make_batch(cfg)
