@@ -557,14 +557,14 @@ __global__ __launch_bounds__(256) void conv_state_out_kernel(const uint16_t* __r
 }
 
 // Decode tail: gate, conv and the carried state and context of a batch in
-// which every request has at most one token, in one launch.  Two waves per
-// request.  The first takes the request's token t (if any): its gate from
+// which every request has at most one token, in one launch.  One block of
+// four waves per request.  The first takes the request's token t (if any): its gate from
 // the h and k rows, the gated row g*v (written to `gated`, the conv input),
 // the conv output, whose older taps all lie before the request start and so
 // come from the carried state (or are zero), and the newest carried state
-// row (the gated row).  The second shifts the carried state by the request's
-// token count (rows 1.. of the old state; all of it for an empty request) and
-// writes the carried context.  The conv's weights, taps and value rows are
+// row (the gated row).  The other three shift the carried state by the
+// request's token count (rows 1.. of the old state; all of it for an empty
+// request), a third each, and write the carried context.  The conv's weights, taps and value rows are
 // loaded with the h and k rows, so the token costs one round trip after the
 // request lookup.  Arithmetic is that of gate_kernel and conv_rows_kernel
 // (token_gate, gate_chunk, conv_chunk), so the results are the same bits.
@@ -575,19 +575,41 @@ __global__ __launch_bounds__(256) void decode_tail_kernel(DecodeTailArgs a) {
     constexpr int G = 4;  // 16-byte chunks per lane per pass
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int r = blockIdx.x * 2 + (wid >> 1);
-    if (r >= a.R) return;  // whole wave
+    const int r = blockIdx.x;
     int64_t ta, tb;
     carried_window(a.qsl, a.T, r, nullptr, ta, tb);
     const int64_t n = tb - ta;
     const int N = a.N, nch = N >> 3;
     const int S = (KC - 1) * a.d;
 
-    if ((wid & 1) == 1) {  // carried state shift and context
-        if (a.state_out != nullptr && S > 0 && n <= 1)
-            for (int m = 0; m < S - (int)n; ++m) carry_state_row(a.gated, a.state, N, S, r, m, ta, tb, a.state_out, lane);
-        if (a.ctx_out != nullptr && lane < a.C)
+    if (wid > 0) {  // waves 1-3: carried state shift (a third each) and context
+        if (wid == 1 && a.ctx_out != nullptr && lane < a.C)
             a.ctx_out[(int64_t)r * a.C + lane] = carried_token(a.tok, a.ctx, a.C, a.eos, r, lane, ta, tb);
+        if (a.state_out != nullptr && S > 0 && n <= 1) {
+            // out rows m < S - n take old rows m + n (zeros without a state):
+            // a flat copy of (S - n) * nch chunks split over the three waves,
+            // 16 in flight per lane
+            constexpr int U = 16;
+            const int all = (S - (int)n) * nch;
+            const int per = (all + 3 * kWave - 1) / (3 * kWave) * kWave;  // whole passes of 64 chunks
+            const int lo = (wid - 1) * per;
+            const int total = min(all, lo + per);
+            const u32x4* src = a.state != nullptr ? (const u32x4*)(a.state + ((int64_t)r * S + n) * N) : nullptr;
+            u32x4* dst = (u32x4*)(a.state_out + (int64_t)r * S * N);
+            for (int base = lo; base < total; base += U * kWave) {
+                u32x4 vv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = base + u * kWave + lane;
+                    vv[u] = (src != nullptr && idx < total) ? src[idx] : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = base + u * kWave + lane;
+                    if (idx < total) dst[idx] = vv[u];
+                }
+            }
+        }
         return;
     }
     if (n != 1) return;
@@ -657,8 +679,8 @@ __global__ __launch_bounds__(256) void decode_tail_kernel(DecodeTailArgs a) {
 
 template <int KC>
 static hipError_t launch_decode_tail_t(const DecodeTailArgs& a, hipStream_t s) {
-    const int64_t blocks = ((int64_t)a.R + 1) / 2;  // two requests (four waves) per block
-    hipLaunchKernelGGL(decode_tail_kernel<KC>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    // one request per block: wave 0 the token, waves 1-3 the state shift
+    hipLaunchKernelGGL(decode_tail_kernel<KC>, dim3((unsigned)a.R), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
