@@ -627,10 +627,11 @@ def bench_spec_decode(args):
     out = torch.empty((T, cfg.N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def verify(s):
+    def verify(s, hint=W):
+        # windows of W <= 4 tokens: the fused entry point's one-kernel tail for gate and conv
         l = s % L
         ple.ple_prefill_fused(layers[l], toks, qsl, hidden, ngram_context=ctx[l][0], conv_state=st[l][0], out=out,
-                              workspace=ws[l])
+                              workspace=ws[l], max_request_tokens=hint)
 
     def commit(s):
         l = s % L
@@ -638,8 +639,8 @@ def bench_spec_decode(args):
                             x=xs[l], conv_kernel=cfg.conv_kernel, conv_dilation=cfg.conv_dilation,
                             conv_state=st[l][0], conv_state_out=st[l][1])
 
-    def step(s):
-        verify(s)
+    def step(s, hint=W):
+        verify(s, hint)
         commit(s)
         l = s % L
         st[l].reverse()
@@ -664,6 +665,15 @@ def bench_spec_decode(args):
         step(s)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    # the same steps with separate gate and conv kernels (no window hint)
+    for s in range(L):
+        step(s, hint=0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s, hint=0)
+    torch.cuda.synchronize()
+    unhinted_ms = (time.perf_counter() - t0) * 1e3 / K
     # The same step as a HIP graph per layer (verify + commit; the library
     # allocates nothing and clears nothing with memset, so the calls capture
     # as plain kernel nodes), replayed the way a serving loop would.
@@ -708,6 +718,7 @@ def bench_spec_decode(args):
                        "context_len": C, "layers_rotated": L},
             "committed_tokens_per_s": round(float(acc_h.sum()) / (eager_ms * 1e-3), 1),
             "graph_ms_per_step": round(ms_per_step, 4),
+            "separate_kernels_ms_per_step": round(unhinted_ms, 4),
             "verify_ms": round(verify_ms, 5),
             "commit": {"ms": round(commit_ms, 5), "bytes": commit_bytes,
                        "GBps": round(commit_bytes / (commit_ms * 1e-3) / 1e9, 1),

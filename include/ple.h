@@ -125,11 +125,12 @@ typedef struct ple_batch_desc {
     const int32_t* query_start_loc;  /* device [R+1] */
     int64_t num_tokens;              /* 0 <= T <= PLE_MAX_TOKENS */
     int32_t num_reqs;                /* R >= 0 (R == 0 requires T == 0) */
-    int32_t max_request_tokens;      /* hint: 0 = unknown; 1 = no request has more than one
-                                        token (decode), which lets ple_prefill_fused run gate,
-                                        conv and the carried state/context as one kernel; a
-                                        wrong hint gives unspecified results for the requests
-                                        that break it (never out-of-bounds accesses) */
+    int32_t max_request_tokens;      /* hint: 0 = unknown; 1..4 = no request has more tokens
+                                        (a decode step, a speculative verify window), which lets
+                                        ple_prefill_fused run gate, conv and the carried
+                                        state/context as one kernel; a wrong hint gives
+                                        unspecified results for the requests that break it
+                                        (never out-of-bounds accesses) */
     const int32_t* ngram_context;    /* device [R][C], oldest first, or NULL (= all EOS) */
     int32_t* ngram_context_out;      /* device [R][C] or NULL: last C raw tokens of
                                         ngram_context[r] ++ request r's tokens; must not
@@ -253,11 +254,12 @@ int ple_conv(const uint16_t* x, const ple_batch_desc* batch, const uint16_t* w, 
  * round256 rounds up to a multiple of 256 and T = batch->num_tokens: a
  * speculative verify step that keeps one workspace per layer passes that
  * region as x to ple_spec_commit.
- * With batch->max_request_tokens == 1 (a decode batch: no request has more
- * than one token) and Kc <= 4, gate, conv and the carried state and context
- * run as one kernel ([P3] 实现拆解 items 2 and 5: the decode-path conv with
- * the state kept by the short-conv backend); every output, the conv input
- * in the workspace included, is the same bits as without the hint.
+ * With batch->max_request_tokens in 1..4 (a decode step or speculative
+ * verify windows: no request has more tokens), Kc <= 4 and N <= 8192, gate,
+ * conv and the carried state and context run as one kernel ([P3] 实现拆解
+ * items 2, 4 and 5: the decode and speculative conv paths with the state
+ * kept by the short-conv backend); every output, the conv input in the
+ * workspace included, is the same bits as without the hint.
  */
 int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
                       const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* workspace,

@@ -298,8 +298,9 @@ def prefill_conv_input(layer: Layer, workspace, num_tokens: int):
 def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefetched_rows=None, ngram_context=None,
                       ngram_context_out=None, conv_state=None, conv_state_out=None, out=None, gate=None,
                       workspace=None, max_request_tokens=0, stream=None):
-    """max_request_tokens: 0 (unknown) or 1 (no request has more than one token: a decode batch,
-    run with one kernel for gate, conv and the carried state and context)."""
+    """max_request_tokens: 0 (unknown) or 1..4 (no request has more tokens: a decode step or
+    speculative verify windows, run with one kernel for gate, conv and the carried state and
+    context)."""
     T, N = hidden.shape
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=hidden.device)

@@ -661,9 +661,9 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
         e = launch_kv_proj(x, layer->kv_weight, T, HD, 2 * N, kv, s);
         if (e != hipSuccess) return hip_fail(e, "kv_proj launch");
     }
-    // decode batches (at most one token per request): gate, conv and the
-    // carried state and context in one launch
-    if (batch->max_request_tokens == 1 && decode_tail_supported(layer->conv_kernel)) {
+    // decode batches and verify windows (at most 4 tokens per request): gate,
+    // conv and the carried state and context in one launch
+    if (decode_tail_supported(batch->max_request_tokens, layer->conv_kernel, N)) {
         DecodeTailArgs a;
         a.hidden = hidden;
         a.kv = kv;

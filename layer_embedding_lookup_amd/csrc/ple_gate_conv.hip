@@ -557,42 +557,48 @@ __global__ __launch_bounds__(256) void conv_state_out_kernel(const uint16_t* __r
 }
 
 // Decode tail: gate, conv and the carried state and context of a batch in
-// which every request has at most one token, in one launch.  One block of
-// four waves per request.  The first takes the request's token t (if any): its gate from
-// the h and k rows, the gated row g*v (written to `gated`, the conv input),
-// the conv output, whose older taps all lie before the request start and so
-// come from the carried state (or are zero), and the newest carried state
-// row (the gated row).  The other three shift the carried state by the
-// request's token count (rows 1.. of the old state; all of it for an empty
-// request), a third each, and write the carried context.  The conv's weights, taps and value rows are
-// loaded with the h and k rows, so the token costs one round trip after the
-// request lookup.  Arithmetic is that of gate_kernel and conv_rows_kernel
-// (token_gate, gate_chunk, conv_chunk), so the results are the same bits.
-// Requests with more than one token are left unwritten (the caller promised
+// which every request has at most kTailTokens tokens (a decode step, or a
+// speculative verify window), in one launch.  One block of eight waves per
+// request.  Wave j < kTailTokens takes the request's token t = a + j (if
+// any): its gate from the h and k rows and the gated row g*v, which it writes
+// to `gated` (the conv input), to the block's LDS and, when it is among the
+// last S inputs, to its carried state row; after a block barrier, its conv
+// output, whose taps inside the window come from the other token waves'
+// gated rows in LDS and whose older taps come from the carried state (or are
+// zero).  Waves 4-7 shift the carried state by the window length (rows n..
+// of the old state), a quarter each, and write the carried context.  The
+// conv's state taps, weights and the value row are loaded with the h and k
+// rows, so a token costs one round trip after the request lookup.
+// Arithmetic is that of gate_kernel and conv_rows_kernel (token_gate,
+// gate_chunk, conv_chunk), so the results are the same bits.  Tokens past
+// the kTailTokens-th of a request are left unwritten (the caller promised
 // none); every access stays in bounds for any query_start_loc.
+constexpr int kTailTokens = 4;
+
 template <int KC>
-__global__ __launch_bounds__(256) void decode_tail_kernel(DecodeTailArgs a) {
+__global__ __launch_bounds__(512) void decode_tail_kernel(DecodeTailArgs a) {
     constexpr int G = 4;  // 16-byte chunks per lane per pass
+    extern __shared__ u32x4 s_gated[];  // [kTailTokens][nch]: the window's gated rows
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int r = blockIdx.x;
     int64_t ta, tb;
     carried_window(a.qsl, a.T, r, nullptr, ta, tb);
-    const int64_t n = tb - ta;
+    const int n = (int)min(tb - ta, (int64_t)(1 << 30));
     const int N = a.N, nch = N >> 3;
     const int S = (KC - 1) * a.d;
 
-    if (wid > 0) {  // waves 1-3: carried state shift (a third each) and context
-        if (wid == 1 && a.ctx_out != nullptr && lane < a.C)
+    if (wid >= kTailTokens) {  // waves 4-7: carried state shift (a quarter each) and context
+        const int cw = wid - kTailTokens;
+        if (cw == 0 && a.ctx_out != nullptr && lane < a.C)
             a.ctx_out[(int64_t)r * a.C + lane] = carried_token(a.tok, a.ctx, a.C, a.eos, r, lane, ta, tb);
-        if (a.state_out != nullptr && S > 0 && n <= 1) {
+        if (a.state_out != nullptr && S > n) {
             // out rows m < S - n take old rows m + n (zeros without a state):
-            // a flat copy of (S - n) * nch chunks split over the three waves,
-            // 16 in flight per lane
+            // a flat copy of (S - n) * nch chunks, 16 in flight per lane
             constexpr int U = 16;
-            const int all = (S - (int)n) * nch;
-            const int per = (all + 3 * kWave - 1) / (3 * kWave) * kWave;  // whole passes of 64 chunks
-            const int lo = (wid - 1) * per;
+            const int all = (S - n) * nch;
+            const int per = (all + 4 * kWave - 1) / (4 * kWave) * kWave;  // whole passes of 64 chunks
+            const int lo = cw * per;
             const int total = min(all, lo + per);
             const u32x4* src = a.state != nullptr ? (const u32x4*)(a.state + ((int64_t)r * S + n) * N) : nullptr;
             u32x4* dst = (u32x4*)(a.state_out + (int64_t)r * S * N);
@@ -610,68 +616,99 @@ __global__ __launch_bounds__(256) void decode_tail_kernel(DecodeTailArgs a) {
                 }
             }
         }
+        __syncthreads();  // every wave of the block meets the token waves' barrier
         return;
     }
-    if (n != 1) return;
-    const int64_t t = ta;
+
+    const int j = wid;  // token slot
+    const bool has = j < n;
+    const int64_t t = has ? ta + j : 0;
     const u32x4* __restrict__ h = (const u32x4*)(a.hidden + t * N);
     const u32x4* __restrict__ k = (const u32x4*)(a.kv + t * 2 * (int64_t)N);
     const u32x4* __restrict__ v = k + nch;
     const u32x4* __restrict__ wc = (const u32x4*)a.conv_w;  // chunk c's weights: KC chunks from c*KC
-    // older tap i (1..KC-1) of chunk c: carried state row S - i*d of request r, or zero
-    auto tap_row = [&](int i) -> const u32x4* {
-        return a.state != nullptr ? (const u32x4*)(a.state + ((int64_t)r * S + (S - i * a.d)) * N) : nullptr;
-    };
-    auto load_pass = [&](int c0, u32x4 (&vv)[G], u32x4 (&xv)[G][KC], u32x4 (&wq)[G][KC]) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int c = c0 + j * kWave + lane;
-            const bool in = c < nch;
-            vv[j] = in ? v[c] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 1; i < KC; ++i) {
-                const u32x4* tr = tap_row(i);
-                xv[j][i] = (in && tr != nullptr) ? tr[c] : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int q = 0; q < KC; ++q) wq[j][q] = in ? wc[(int64_t)c * KC + q] : u32x4{0u, 0u, 0u, 0u};
-        }
+    // tap i (1..KC-1) of this token: inside the window (slot j - i*d of the
+    // block's LDS) or before it (carried state row S - (i*d - j), or zero)
+    auto state_tap = [&](int i) -> const u32x4* {
+        const int back = i * a.d - j;  // rows before the request start
+        return (back > 0 && a.state != nullptr) ? (const u32x4*)(a.state + ((int64_t)r * S + (S - back)) * N)
+                                                : nullptr;
     };
     u32x4 vv[G], xv[G][KC], wq[G][KC];
-    load_pass(0, vv, xv, wq);  // independent of the gate: in flight with h and k
+    auto load_pass = [&](int c0) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int c = c0 + q * kWave + lane;
+            const bool in = has && c < nch;
+            vv[q] = in ? v[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 1; i < KC; ++i) {
+                const u32x4* tr = state_tap(i);
+                xv[q][i] = (in && tr != nullptr) ? tr[c] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int w = 0; w < KC; ++w) wq[q][w] = in ? wc[(int64_t)c * KC + w] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    const bool one_pass = nch <= G * kWave;
+    if (one_pass) load_pass(0);  // independent of the gate: in flight with h and k
 
     // per-lane partial sums in gate_kernel's order (chunks lane, lane+64, ...)
     constexpr int UNROLL = 8;
     float hh = 0.f, kk = 0.f, hk = 0.f;
-    for (int base = lane; base < nch; base += 64 * UNROLL) {
-        u32x4 hv[UNROLL], kv4[UNROLL];
+    if (has) {
+        for (int base = lane; base < nch; base += 64 * UNROLL) {
+            u32x4 hv[UNROLL], kv4[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int idx = base + 64 * u;
-            if (idx < nch) {
-                hv[u] = h[idx];
-                kv4[u] = k[idx];
+            for (int u = 0; u < UNROLL; ++u) {
+                const int idx = base + 64 * u;
+                if (idx < nch) {
+                    hv[u] = h[idx];
+                    kv4[u] = k[idx];
+                }
             }
-        }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            if (base + 64 * u < nch) acc_dot(hv[u], kv4[u], hh, kk, hk);
+            for (int u = 0; u < UNROLL; ++u)
+                if (base + 64 * u < nch) acc_dot(hv[u], kv4[u], hh, kk, hk);
+        }
     }
     const float g = token_gate(hh, kk, hk, N, a.eps);
-    if (lane == 0 && a.gate != nullptr) a.gate[t] = g;
+    if (has && lane == 0 && a.gate != nullptr) a.gate[t] = g;
+    // the newest carried state rows are the window's last S gated rows
+    const int srow = j + S - n;
+    uint16_t* st_row = (has && a.state_out != nullptr && srow >= 0 && srow < S)
+                           ? a.state_out + ((int64_t)r * S + srow) * N
+                           : nullptr;
 
+    // gated rows: to memory, LDS and the carried state
     for (int c0 = 0; c0 < nch; c0 += G * kWave) {
-        if (c0 > 0) load_pass(c0, vv, xv, wq);
+        if (!one_pass) load_pass(c0);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int c = c0 + j * kWave + lane;
-            if (c < nch) {
-                const u32x4 gv = gate_chunk(g, vv[j]);
-                xv[j][0] = gv;
+        for (int q = 0; q < G; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (has && c < nch) {
+                const u32x4 gv = gate_chunk(g, vv[q]);
+                s_gated[j * nch + c] = gv;
                 ((u32x4*)(a.gated + t * N))[c] = gv;
-                if (a.state_out != nullptr && S > 0)
-                    ((u32x4*)(a.state_out + ((int64_t)r * S + (S - 1)) * N))[c] = gv;
-                ((u32x4*)(a.y + t * N))[c] = conv_chunk<KC>(wq[j], xv[j]);
+                if (st_row != nullptr) ((u32x4*)st_row)[c] = gv;
+            }
+        }
+    }
+    __syncthreads();
+    // conv: tap 0 is this token, taps inside the window from LDS
+    for (int c0 = 0; c0 < nch; c0 += G * kWave) {
+        if (!one_pass) load_pass(c0);
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (has && c < nch) {
+                u32x4 x[KC];
+#pragma unroll
+                for (int i = 0; i < KC; ++i) {
+                    const int slot = j - i * a.d;
+                    x[i] = slot >= 0 ? s_gated[slot * nch + c] : xv[q][i];
+                }
+                ((u32x4*)(a.y + t * N))[c] = conv_chunk<KC>(wq[q], x);
             }
         }
     }
@@ -679,12 +716,19 @@ __global__ __launch_bounds__(256) void decode_tail_kernel(DecodeTailArgs a) {
 
 template <int KC>
 static hipError_t launch_decode_tail_t(const DecodeTailArgs& a, hipStream_t s) {
-    // one request per block: wave 0 the token, waves 1-3 the state shift
-    hipLaunchKernelGGL(decode_tail_kernel<KC>, dim3((unsigned)a.R), dim3(256), 0, s, a);
+    // one request per block: waves 0-3 its tokens, waves 4-7 the state shift
+    const size_t lds = (size_t)kTailTokens * (size_t)a.N * 2;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)decode_tail_kernel<KC>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(decode_tail_kernel<KC>, dim3((unsigned)a.R), dim3(512), lds, s, a);
     return hipGetLastError();
 }
 
-bool decode_tail_supported(int K) { return K >= 1 && K <= 4; }
+bool decode_tail_supported(int max_request_tokens, int K, int N) {
+    return max_request_tokens >= 1 && max_request_tokens <= kTailTokens && K >= 1 && K <= 4 &&
+           (size_t)kTailTokens * (size_t)N * 2 <= 64 * 1024;
+}
 
 hipError_t launch_decode_tail(const DecodeTailArgs& a, int K, hipStream_t s) {
     if (a.R <= 0) return hipSuccess;

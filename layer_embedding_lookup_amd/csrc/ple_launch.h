@@ -48,8 +48,9 @@ hipError_t launch_select_rows(const uint16_t* gathered, int E, int64_t slot, int
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s);
 
-// Gate, conv and carried state/context for batches of at most one token per
-// request (decode), one launch; K = conv kernel size (decode_tail_supported).
+// Gate, conv and carried state/context for batches of at most a few tokens
+// per request (decode, speculative verify windows), one launch; K = conv
+// kernel size (decode_tail_supported).
 struct DecodeTailArgs {
     const uint16_t* hidden;  // [T][N]
     const uint16_t* kv;      // [T][2N]
@@ -71,7 +72,7 @@ struct DecodeTailArgs {
     uint16_t* y;             // [T][N]
     float* gate;             // [T] or NULL
 };
-bool decode_tail_supported(int K);
+bool decode_tail_supported(int max_request_tokens, int K, int N);
 hipError_t launch_decode_tail(const DecodeTailArgs& a, int K, hipStream_t s);
 
 hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, uint16_t* out,

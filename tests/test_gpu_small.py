@@ -488,23 +488,39 @@ def _run_fused_both(cfg, b, L, hidden, *, with_ctx, with_state, max_request_toke
 
 
 @pytest.mark.parametrize("case", ["decode-256", "decode-256-fresh", "tiny-empty-requests-k4", "tiny-k1", "tiny-k2",
-                                  "tiny-k3-fresh", "all-empty"])
+                                  "tiny-k3-fresh", "all-empty", "windows-256x4", "windows-256x4-fresh",
+                                  "tiny-windows-k4-d2", "tiny-windows-k2-d1", "tiny-windows-k3-d1-fresh",
+                                  "tiny-windows-k4-d3"])
 def test_decode_tail_equals_plain_path(case):
-    """With max_request_tokens = 1 the fused entry point runs gate, conv and the carried state and
-    context as one kernel; every output is the same bits as the separate kernels' (same arithmetic),
-    including the conv input left in the workspace, on batches of one-token and empty requests."""
+    """With max_request_tokens = 1..4 (decode steps, speculative verify windows) the fused entry point
+    runs gate, conv and the carried state and context as one kernel; every output is the same bits as
+    the separate kernels' (same arithmetic), including the conv input left in the workspace, on
+    batches of one-token, window and empty requests (taps inside and before the window)."""
     import dataclasses
-    if case.startswith("decode-256"):
+    hint = 4 if "windows" in case else 1
+    if case.startswith("decode-256") or case.startswith("windows-256"):
         cfg = wl.CONFIGS[2]
         b = wl.make_batch(cfg, with_context=True, with_state=True)
         K = cfg.conv_kernel
+        if case.startswith("windows"):
+            W = 4
+            cfg = dataclasses.replace(cfg, T=cfg.T * W)
+            b = dataclasses.replace(b, cfg=cfg, input_ids=wl.make_tokens(cfg, T=cfg.T),
+                                    qsl=np.arange(0, cfg.T + 1, W, dtype=np.int32))
     else:
         base = wl.CONFIGS[1]
-        K = {"tiny-empty-requests-k4": 4, "tiny-k1": 1, "tiny-k2": 2, "tiny-k3-fresh": 3, "all-empty": 4}[case]
-        lens = [0, 0, 0] if case == "all-empty" else [1, 0, 1, 1, 0, 0, 1, 1, 0, 1]
-        cfg = dataclasses.replace(base, idx=60, T=int(sum(lens)), conv_kernel=K)
+        K = int(case.split("-k")[1][0]) if "-k" in case else 4
+        d = int(case.split("-d")[1][0]) if "-d" in case else base.conv_dilation
+        rng = np.random.default_rng(61 + K + 7 * d)
+        if case == "all-empty":
+            lens = [0, 0, 0]
+        elif "windows" in case:
+            lens = [int(x) for x in rng.integers(0, 5, size=12)]
+            lens[0], lens[1] = 4, 0
+        else:
+            lens = [1, 0, 1, 1, 0, 0, 1, 1, 0, 1]
+        cfg = dataclasses.replace(base, idx=60, T=int(sum(lens)), conv_kernel=K, conv_dilation=d)
         b = wl.make_batch(base, with_context=True, with_state=True)
-        rng = np.random.default_rng(61 + K)
         R = len(lens)
         qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
         S = (K - 1) * cfg.conv_dilation
@@ -517,9 +533,9 @@ def test_decode_tail_equals_plain_path(case):
     cw = wl.normal_bf16((cfg.N, K), 63 + K, 0.3)
     L = ple.Layer(hash_params(b), tb, dev_bf16(kvw), dev_bf16(cw), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
     hidden = wl.make_hidden(cfg, T=max(cfg.T, 1))[:cfg.T]
-    log(f"decode tail {case}: T={cfg.T} R={b.R} K={K}")
+    log(f"decode tail {case}: T={cfg.T} R={b.R} K={K} d={cfg.conv_dilation} hint={hint}")
     plain = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=0)
-    tail = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=1)
+    tail = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=hint)
     for name, x, y in zip(["out", "gate", "conv input", "state out", "context out"], plain, tail):
         np.testing.assert_array_equal(y, x, err_msg=name)
     if case == "decode-256":  # and against the oracle
