@@ -724,6 +724,36 @@ def test_prefetch_dedup_equals_prefetch(variant):
         assert int(nu.item()) < ids.size // 2
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8-global", "nvfp4"])
+def test_prefetch_dedup_rows_of_512(fmt):
+    """The deduplicating prefetch on 512-element rows (the scalar-address row stream for fp8 and NVFP4,
+    with the repeated rows skipped by its masked stores) equals the plain prefetch, bit for bit."""
+    import dataclasses
+    base = wl.CONFIGS[4] if fmt.startswith("fp8") else wl.CONFIGS[3]
+    cfg = dataclasses.replace(base, idx=41, T=700, vocab_base=5003)
+    b = wl.make_batch(cfg)
+    if fmt == "nvfp4":
+        codes, bs, t = wl.make_nvfp4_table(cfg.num_rows, cfg.D, cfg.seed)
+        tb, keep = _nvfp4_dev(codes, bs, t)
+    elif fmt == "fp8-global":
+        q, _ = wl.make_table(cfg)
+        keep = (dev(q), dev(np.asarray([0.0173], np.float32)))
+        tb = ple.Table.from_tensor(*keep)
+    else:
+        _, _, tb, keep = _table_dev(cfg)
+    L = ple.Layer(hash_params(b), tb, dev_bf16(wl.make_kv_weight(cfg)), dev_bf16(wl.make_conv_weight(cfg)),
+                  conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    d_toks, d_qsl = dev(b.input_ids), dev(b.qsl)
+    plain = torch.empty((cfg.T, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+    ple.ple_prefetch(L, d_toks, d_qsl, plain)
+    staging = torch.full_like(plain, float("nan"))
+    nu = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    ple.ple_prefetch_dedup(L, d_toks, d_qsl, staging, num_unique=nu)
+    assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
+    ids = oracle_ids(b)
+    assert int(nu.item()) == len(np.unique(ids)) < ids.size  # the Zipf batch repeats rows
+
+
 def test_prefetch_dedup_empty_batch_counts_zero():
     cfg = wl.CONFIGS[1]
     b = wl.make_batch(cfg)
