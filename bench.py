@@ -54,7 +54,7 @@ def main() -> int:
                          "sharded table, and the decode and speculative-decode steps of the decode-shaped model")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         return 2
 
