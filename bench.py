@@ -177,6 +177,12 @@ def main() -> int:
         "conv": timed(lambda i: ple.ple_conv(gated, qsl, conv_w, dilation=cfg.conv_dilation, y=out), reps),
     }
     lookup_ms = stage_ms["lookup"]
+    # reference point for kv_proj: the vendor GEMM (torch.matmul, which calls
+    # hipBLASLt) on the same rows and weights, then ours again, so that the
+    # chip's clock drift under sustained MFMA load shows in the pair
+    torch.matmul(rows, kv_ws[0].t(), out=kv)  # first call loads the kernel
+    vendor_kv_ms = timed(lambda i: torch.matmul(rows, kv_ws[i % 4].t(), out=kv), reps)
+    kv_again_ms = timed(lambda i: ple.ple_kv_proj(rows, kv_ws[i % 4], kv=kv), reps)
     # the same launches into one output buffer, as inside the fused step (its
     # workspace rows are rewritten every layer)
     lookup_same_ms = timed(lambda i: ple.ple_lookup(hashes[i % L], tb, toks, qsl, rows=rows), 4 * L)
@@ -249,6 +255,8 @@ def main() -> int:
                    "same_output_frac_hbm_peak": round(lookup_bytes / (lookup_same_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                    "write_only_ms": round(write_only_ms, 5),
                    "torch_index_select_ms": None if torch_gather_ms is None else round(torch_gather_ms, 5)},
+        "kv_proj": {"ms": round(stage_ms["kv_proj"], 5), "ms_after_vendor": round(kv_again_ms, 5),
+                    "torch_matmul_ms": round(vendor_kv_ms, 5), "flops": kv_flops},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_GBps": {"gate": round(gate_bytes / (stage_ms["gate"] * 1e-3) / 1e9, 1),
                         "conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)},
