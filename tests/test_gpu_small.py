@@ -311,7 +311,10 @@ def _check_kv(got, want, x, w):
                                    # 256 x 256 tile kernel (>= 256 tiles): 1 to 5 K-slices of 64,
                                    # ragged in M and in O
                                    (4100, 128, 4112), (4103, 256, 4096), (64, 64, 65536), (2048, 192, 8192),
-                                   (2100, 320, 8208)])
+                                   (2100, 320, 8208),
+                                   # 512 and more 256 x 256 tiles (two or more per CU): whole tiles, an
+                                   # uneven 522-tile split
+                                   (4096, 704, 8192), (4608, 768, 7424), (8192, 1024, 4096)])
 def test_kv_proj_parity(M, K, O):
     log(f"kv_proj M={M} K={K} O={O}")
     x = wl.normal_bf16((M, K), 100 + M, 0.02)
