@@ -225,7 +225,8 @@ def main() -> int:
                            args.workload)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "prefill-8k-bf16-hbm"
+        else METRIC.replace("8k-token prefill", f"{T // 1024}k-token prefill, {fmt} table"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
