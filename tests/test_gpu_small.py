@@ -546,6 +546,43 @@ def test_decode_tail_equals_plain_path(case):
         assert np.abs(bf16_f64(tail[0]) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
 
 
+def test_wrong_hint_keeps_short_requests_exact():
+    """A max_request_tokens hint smaller than the batch's longest request gives unspecified results for
+    the longer requests but stays within every buffer: the call succeeds, and requests of at most four
+    tokens (the tail kernel's token slots) come out exactly as on the plain path, as does every carried
+    context.  Requests of 7, 1, 13, 3, 0 and 2 tokens with the hint 2."""
+    import dataclasses
+    base = wl.CONFIGS[1]
+    lens = [7, 1, 13, 3, 0, 2]
+    rng = np.random.default_rng(91)
+    cfg = dataclasses.replace(base, idx=61, T=int(sum(lens)))
+    b = wl.make_batch(base, with_context=True, with_state=True)
+    R = len(lens)
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    S = (cfg.conv_kernel - 1) * cfg.conv_dilation
+    b = dataclasses.replace(b, cfg=cfg, input_ids=rng.integers(0, 1000, size=cfg.T).astype(np.int32), qsl=qsl,
+                            ngram_context=rng.integers(0, 1000, size=(R, cfg.context_len)).astype(np.int32),
+                            conv_state=wl.normal_bf16((R, S, cfg.N), 92, 0.125))
+    table, scales, tb, keep = _table_dev(cfg)
+    L = ple.Layer(hash_params(b), tb, dev_bf16(wl.make_kv_weight(cfg)), dev_bf16(wl.normal_bf16((cfg.N, 4), 93, 0.3)),
+                  conv_dilation=cfg.conv_dilation, eps=cfg.eps)
+    hidden = wl.make_hidden(cfg, T=cfg.T)
+    log(f"wrong hint: lens={lens} hint=2")
+    plain = _run_fused_both(cfg, b, L, hidden, with_ctx=True, with_state=True, max_request_tokens=0)
+    hinted = _run_fused_both(cfg, b, L, hidden, with_ctx=True, with_state=True, max_request_tokens=2)
+    np.testing.assert_array_equal(hinted[4], plain[4], err_msg="context out")
+    checked = 0
+    for r, n in enumerate(lens):
+        if n > 4:
+            continue
+        rows = slice(qsl[r], qsl[r + 1])
+        for name, i in (("out", 0), ("gate", 1), ("conv input", 2)):
+            np.testing.assert_array_equal(hinted[i][rows], plain[i][rows], err_msg=f"{name}, request {r}")
+        np.testing.assert_array_equal(hinted[3][r], plain[3][r], err_msg=f"state out, request {r}")
+        checked += 1
+    assert checked == 4
+
+
 def test_prefill_with_prefetched_rows_equals_plain():
     cfg = wl.CONFIGS[2]
     b = wl.make_batch(cfg)
