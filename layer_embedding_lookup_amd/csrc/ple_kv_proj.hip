@@ -83,6 +83,9 @@ constexpr int kBigThreads = 256;
 constexpr int kBBK = 64;
 constexpr int kNStage = 2;
 constexpr int kBigMaxK = 1 << 20;  // keeps 256 rows of K bf16 within a 32-bit buffer offset
+#ifndef PLE_KV_WIDE
+#define PLE_KV_WIDE 1  // 256-wide tiles: eight waves of 128 x 64 on 16x16x32 MFMAs
+#endif
 
 // Block tile BT x BT (256, or 128 / 64 for problems too small to fill the
 // chip with wider tiles); each of the 4 waves holds a (BT/2) x (BT/2) block
@@ -357,6 +360,153 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
         if (gr < M && gc < O) *(u32x4*)(out + (int64_t)gr * O + gc) = *(const u32x4*)(Cs + row * P::OUT_ROW + col);
     }
 }
+
+// ---------------------------------------------------------------------------
+// 256-wide tiles with eight waves (two per SIMD) on 16x16x32 MFMAs: wave
+// (wm, wn) holds a 128 x 64 block (x rows wm*128.., W rows wn*64..) as 8 x 4
+// accumulator tiles of 16 x 16 (128 accumulation registers), so a wave
+// waiting on its fragments leaves the matrix core to the other wave of its
+// SIMD.  LDS layout, copies and slice pipeline as the four-wave body; a slice
+// is two K-steps of 32 with 12 fragment reads each.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 512;
+struct Frag8w {
+    u32x4 a[8], b[4];
+};
+#define PLE_FRAG8W_REGS(f)                                                                                       \
+    "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]), "+v"(f.a[7]), \
+        "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3])
+
+__device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M,
+                                               int K, int O, uint16_t* __restrict__ out) {
+    using P = PipeShape<256>;
+    constexpr int BT = 256, NC = 4;  // copy instructions per operand, wave and slice
+    extern __shared__ __align__(16) char lds_raw[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int tiles_m = (M + BT - 1) / BT;
+    const int tiles_n = (O + BT - 1) / BT;
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BT, n0 = tn * BT;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (int64_t)m0 * K), (short)0, min(M - m0, BT) * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w + (int64_t)n0 * K), (short)0, min(O - n0, BT) * K * 2, 0x00020000);
+    // copy instruction i of wave `wave` fills rows g*8 .. g*8+7, g = i*8 + wave
+    uint32_t aoff[NC], boff[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int row = (i * 8 + wave) * 8 + (lane >> 3);
+        const int kc = (lane & 7) ^ ((row >> 1) & 7);
+        aoff[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * K * 2 + kc * 16);
+        boff[i] = (uint32_t)((min(n0 + row, O - 1) - n0) * K * 2 + kc * 16);
+    }
+    const int nk = K / kBBK;
+    auto copy_one = [&](int kt, int i) {
+        char* base = lds_raw + (kt & 1) * P::STAGE_BYTES + (i * 8 + wave) * 1024;
+        const int ko = min(kt, nk - 1) * kBBK * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)base, 16, aoff[i], ko, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + P::OP_BYTES), 16, boff[i], ko, 0, 0);
+    };
+
+    f32x4 acc[4][8];  // [W block jb][x block ib]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int fk = lane >> 4;
+    const int sw = (frow >> 1) & 7;
+    uint32_t a_addr[2], b_addr[2];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_raw;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t col = (uint32_t)(((ks * 4 + fk) ^ sw) * 16);
+        a_addr[ks] = lds_base + (wm * 128 + frow) * 128 + col;
+        b_addr[ks] = lds_base + P::OP_BYTES + (wn * 64 + frow) * 128 + col;
+    }
+    auto read_one = [&](int q, int kt, int ks, Frag8w& f) {
+        const uint32_t so = (uint32_t)(kt & 1) * P::STAGE_BYTES;
+        const uint32_t pa = a_addr[ks] + so, pb = b_addr[ks] + so;
+        switch (q) {
+            case 0: asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[0]) : "v"(pa)); break;
+            case 1: asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(f.a[1]) : "v"(pa)); break;
+            case 2: asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(f.a[2]) : "v"(pa)); break;
+            case 3: asm volatile("ds_read_b128 %0, %1 offset:6144" : "=v"(f.a[3]) : "v"(pa)); break;
+            case 4: asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(f.a[4]) : "v"(pa)); break;
+            case 5: asm volatile("ds_read_b128 %0, %1 offset:10240" : "=v"(f.a[5]) : "v"(pa)); break;
+            case 6: asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(f.a[6]) : "v"(pa)); break;
+            case 7: asm volatile("ds_read_b128 %0, %1 offset:14336" : "=v"(f.a[7]) : "v"(pa)); break;
+            case 8: asm volatile("ds_read_b128 %0, %1" : "=v"(f.b[0]) : "v"(pb)); break;
+            case 9: asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(f.b[1]) : "v"(pb)); break;
+            case 10: asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(f.b[2]) : "v"(pb)); break;
+            default: asm volatile("ds_read_b128 %0, %1 offset:6144" : "=v"(f.b[3]) : "v"(pb)); break;
+        }
+    };
+    auto wait_frag = [&](Frag8w& f) { asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG8W_REGS(f)); };
+    auto wait_barrier = [&](Frag8w& f) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG8W_REGS(f) : : "memory");
+    };
+    // one K-step of 32: 32 MFMAs on cur; after MFMA t < 12, fragment read t of
+    // (rkt, rks) into nxt; with ckt >= 0, the NC copy pairs of slice ckt after
+    // MFMAs 2, 10, 18, 26
+    auto kstep = [&](const Frag8w& cur, Frag8w& nxt, int rkt, int rks, int ckt) {
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int j = t / 8, i = t % 8;
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.b[j]),
+                                                                __builtin_bit_cast(bf16x8, cur.a[i]), acc[j][i], 0, 0,
+                                                                0);
+            if (t < 12) read_one(t, rkt, rks, nxt);
+            if (ckt >= 0 && t % 8 == 2) copy_one(ckt, t / 8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    Frag8w f0, f1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < NC; ++i) copy_one(k, i);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"(2 * NC) : "memory");
+#pragma unroll
+    for (int q = 0; q < 12; ++q) read_one(q, 0, 0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_frag(f0);
+        kstep(f0, f1, kt, 1, -1);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_barrier(f1);  // slice kt+1 has landed; every read of stage kt is done
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(f1, f0, kt + 1, 0, kt + 2);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // acc[jb][ib][e]: feature n0 + wn*64 + jb*16 + 4*fk + e of token m0 + wm*128 + ib*16 + frow
+    uint16_t* Cs = (uint16_t*)lds_raw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int m = wm * 128 + i * 16 + frow;
+            const int o = wn * 64 + j * 16 + 4 * fk;
+            *(uint2*)(Cs + m * P::OUT_ROW + o) =
+                make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]), pack_bf16x2(acc[j][i][2], acc[j][i][3]));
+        }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = tid; c < BT * BT / 8; c += kWideThreads) {
+        const int row = c / (BT / 8);
+        const int col = (c % (BT / 8)) * 8;
+        const int gr = m0 + row, gc = n0 + col;
+        if (gr < M && gc < O) *(u32x4*)(out + (int64_t)gr * O + gc) = *(const u32x4*)(Cs + row * P::OUT_ROW + col);
+    }
+}
+#undef PLE_FRAG8W_REGS
+
 #undef PLE_FRAG_REGS4
 #undef PLE_FRAG_REGS2
 #undef PLE_FRAG_REGS1
@@ -367,6 +517,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void kv_proj_big_kernel(const uint1
                                                                      const uint16_t* __restrict__ w, int M, int K,
                                                                      int O, uint16_t* __restrict__ out) {
     kv_proj_pipe<256>(x, w, M, K, O, out);
+}
+__global__ __launch_bounds__(kWideThreads, 1) void kv_proj_wide_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ w, int M, int K,
+                                                                       int O, uint16_t* __restrict__ out) {
+    kv_proj_pipe8w(x, w, M, K, O, out);
 }
 __global__ __launch_bounds__(kBigThreads, 1) void kv_proj_mid_kernel(const uint16_t* __restrict__ x,
                                                                      const uint16_t* __restrict__ w, int M, int K,
@@ -406,6 +561,15 @@ hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K
     // the widest block tile that still gives 256 blocks
     if (K > kBigMaxK) return hipErrorInvalidValue;  // rejected by the argument checks before this
     const int64_t big_tiles = ((M + 255) / 256) * ((O + 255) / 256);
+    if (PLE_KV_WIDE && big_tiles >= 256) {
+        using P = PipeShape<256>;
+        static const hipError_t attr = hipFuncSetAttribute((const void*)kv_proj_wide_kernel,
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS_BYTES);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(kv_proj_wide_kernel, dim3((unsigned)big_tiles), dim3(kWideThreads), P::LDS_BYTES, s, x, w,
+                           (int)M, K, O, kv);
+        return hipGetLastError();
+    }
     if (big_tiles >= 256) return launch_kv_proj_pipe<256>(x, w, M, K, O, kv, s);
     // (64-wide tiles take 128 KiB of LDS, so only while one block per CU covers them)
     const int64_t mid_tiles = ((M + 127) / 128) * ((O + 127) / 128);
