@@ -6,10 +6,12 @@
 //
 // x [M][K] (gathered rows, K = H*D) and W [O][K] are both K-contiguous, so
 // every lane's MFMA operand (8 consecutive bf16 along K) is one 16-byte read
-// for both sides.  One pipelined kernel body, instantiated for 256 x 256
-// block tiles (problems with at least 256 of them), 128 x 128 tiles (a
-// 1024-token speculative-verify batch) and 64 x 64 tiles (decode batches);
-// its design is described above the body.  The block tile is the largest
+// for both sides.  Problems with at least 256 tiles of 256 x 256 run on
+// eight waves of 128 x 64 with 16x16x32 MFMAs (kv_proj_pipe8w, two waves per
+// SIMD); smaller ones on one four-wave pipelined body of 32x32x16 MFMAs at
+// 128 x 128 tiles (a 1024-token speculative-verify batch) or 64 x 64 tiles
+// (decode batches), which PLE_KV_WIDE=0 also uses for the 256-wide tiles.
+// The designs are described above the bodies.  The block tile is the largest
 // that still gives 256 blocks, one per CU.  Blocks are numbered so that the blocks resident on one XCD (block id
 // mod 8 picks the XCD) work on neighbouring tiles and share their x and W
 // panels in that XCD's L2.
