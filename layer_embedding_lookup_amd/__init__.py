@@ -30,7 +30,7 @@ __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_l
            "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes", "ple_dp_gather_slot", "ple_head_shard",
            "ple_select_rows",
            "ple_kv_proj", "ple_gate", "ple_conv", "ple_spec_commit", "ple_prefill_fused", "ple_prefill_workspace_bytes",
-           "prefill_conv_input",
+           "prefill_conv_input", "prefill_kv",
            "ple_host_alloc", "ple_host_free", "HostBuffer", "ple_stream_create_cu_masked", "ple_stream_destroy",
            "ple_error_message", "ple_version", "library"]
 
@@ -47,6 +47,59 @@ def _ptr(t) -> int | None:
     if not t.is_contiguous():
         raise ValueError("tensor arguments must be contiguous")
     return t.data_ptr()
+
+
+# Host-side checks of the tensors behind the pointers, run before any library
+# call: a mismatched shape would otherwise become an out-of-bounds device
+# access.  Raw integer addresses are passed through unchecked (the caller
+# vouches for them).
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_BYTES = (torch.uint8, torch.int8)
+
+
+def _req(name: str, t, shape, dtypes, *, optional: bool = False):
+    """Check one tensor argument: dtype, exact shape (None = any size on that
+    axis), contiguity.  Returns the tensor."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if len(t.shape) != len(shape) or any(want is not None and int(got) != int(want)
+                                         for got, want in zip(t.shape, shape)):
+        want = ", ".join("*" if w is None else str(int(w)) for w in shape)
+        want = f"({want},)" if len(shape) == 1 else f"({want})"
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _req_bytes(name: str, t, nbytes: int):
+    """A workspace: a contiguous byte tensor of at least nbytes."""
+    if isinstance(t, int):
+        return t
+    _req(name, t, (None,), _BYTES)
+    if t.numel() < nbytes:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {nbytes} needed")
+    return t
+
+
+def _same_device(*tensors):
+    """Every tensor argument on one GPU (raw addresses and None are skipped)."""
+    devs = {(t.device.type, t.device.index) for t in tensors if isinstance(t, torch.Tensor)}
+    for typ, _ in devs:
+        if typ != "cuda":
+            raise ValueError("tensor arguments must be GPU tensors")
+    if len(devs) > 1:
+        raise ValueError(f"tensor arguments are on different devices: {sorted(devs)}")
 
 
 def _stream(stream) -> int | None:
@@ -125,9 +178,11 @@ class Layer:
     def __init__(self, hash: HashParams, table: Table, kv_weight: torch.Tensor, conv_weight: torch.Tensor, *,
                  conv_dilation: int, eps: float = 1e-6):
         self.hash, self.table = hash, table
-        self.kv_weight, self.conv_weight = kv_weight, conv_weight
+        _req("conv_weight", conv_weight, (None, None), _BF16)
         self.hidden = int(conv_weight.shape[0])
         self.conv_kernel = int(conv_weight.shape[1])
+        _req("kv_weight", kv_weight, (2 * self.hidden, hash.num_heads * table.dim), _BF16)
+        self.kv_weight, self.conv_weight = kv_weight, conv_weight
         self.conv_dilation = int(conv_dilation)
         self.eps = float(eps)
 
@@ -137,15 +192,31 @@ class Layer:
 
 
 def _batch(input_ids, query_start_loc, ngram_context=None, ngram_context_out=None, conv_state=None,
-           conv_state_out=None, num_tokens=None, max_request_tokens=0) -> capi.ple_batch_desc:
+           conv_state_out=None, num_tokens=None, max_request_tokens=0, context_len=None,
+           state_shape=None) -> capi.ple_batch_desc:
+    """The batch descriptor, after checking its tensors: input_ids int32 [T],
+    query_start_loc int32 [R+1], contexts int32 [R][context_len], conv states
+    bf16 state_shape = (S, N) per request."""
+    if input_ids is not None:
+        _req("input_ids", input_ids, (None,), _I32)
+    _req("query_start_loc", query_start_loc, (None,), _I32)
     T = int(input_ids.shape[0]) if input_ids is not None else int(num_tokens)
     R = int(query_start_loc.shape[0]) - 1
+    if R < 0:
+        raise ValueError("query_start_loc needs at least one entry")
+    for name, c in (("ngram_context", ngram_context), ("ngram_context_out", ngram_context_out)):
+        if c is not None:
+            if context_len is None:
+                raise ValueError(f"{name} given without the hash's context length")
+            _req(name, c, (R, context_len), _I32)
+    for name, c in (("conv_state", conv_state), ("conv_state_out", conv_state_out)):
+        if c is not None:
+            if state_shape is None:
+                raise ValueError(f"{name} given without the conv shape")
+            _req(name, c, (R, *state_shape), _BF16)
+    _same_device(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out)
     return capi.ple_batch_desc(_ptr(input_ids), _ptr(query_start_loc), T, R, int(max_request_tokens),
                                _ptr(ngram_context), _ptr(ngram_context_out), _ptr(conv_state), _ptr(conv_state_out))
-
-
-def _device_of(t: torch.Tensor) -> torch.device:
-    return t.device
 
 
 def ple_ngram_ids(hash: HashParams, input_ids, query_start_loc, *, ngram_context=None, ngram_context_out=None,
@@ -153,17 +224,22 @@ def ple_ngram_ids(hash: HashParams, input_ids, query_start_loc, *, ngram_context
     T = input_ids.shape[0]
     if ids is None:
         ids = torch.empty((T, hash.num_heads), dtype=torch.int32, device=input_ids.device)
+    _req("ids", ids, (T, hash.num_heads), _I32)
     h = hash.desc()
-    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, context_len=hash.context_len)
+    _same_device(input_ids, ids)
     capi.check(capi.load().ple_ngram_ids(ctypes.byref(h), ctypes.byref(b), _ptr(ids), _stream(stream)),
                "ple_ngram_ids")
     return ids
 
 
 def ple_gather(table: Table, ids, *, rows=None, stream=None):
+    _req("ids", ids, (None, None), _I32)
     T, H = ids.shape
     if rows is None:
         rows = torch.empty((T, H * table.dim), dtype=torch.bfloat16, device=ids.device)
+    _req("rows", rows, (T, H * table.dim), _BF16)
+    _same_device(ids, rows)
     t = table.desc()
     capi.check(capi.load().ple_gather(ctypes.byref(t), _ptr(ids), T, H, _ptr(rows), _stream(stream)), "ple_gather")
     return rows
@@ -171,11 +247,15 @@ def ple_gather(table: Table, ids, *, rows=None, stream=None):
 
 def ple_lookup(hash: HashParams, table: Table, input_ids, query_start_loc, *, ngram_context=None,
                ngram_context_out=None, ids_out=None, rows=None, stream=None):
+    _req("input_ids", input_ids, (None,), _I32)
     T = input_ids.shape[0]
     if rows is None:
         rows = torch.empty((T, hash.num_heads * table.dim), dtype=torch.bfloat16, device=input_ids.device)
+    _req("rows", rows, (T, hash.num_heads * table.dim), _BF16)
+    _req("ids_out", ids_out, (T, hash.num_heads), _I32, optional=True)
     h, t = hash.desc(), table.desc()
-    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, context_len=hash.context_len)
+    _same_device(input_ids, rows, ids_out)
     capi.check(capi.load().ple_lookup(ctypes.byref(h), ctypes.byref(t), ctypes.byref(b), _ptr(ids_out), _ptr(rows),
                                       _stream(stream)), "ple_lookup")
     return rows
@@ -183,8 +263,11 @@ def ple_lookup(hash: HashParams, table: Table, input_ids, query_start_loc, *, ng
 
 def ple_prefetch(layer: Layer, input_ids, query_start_loc, staging, *, ngram_context=None, ngram_context_out=None,
                  stream=None):
+    _req("input_ids", input_ids, (None,), _I32)
+    _req("staging", staging, (input_ids.shape[0], layer.hash.num_heads * layer.table.dim), _BF16)
     L = layer.desc()
-    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, context_len=layer.hash.context_len)
+    _same_device(input_ids, staging)
     capi.check(capi.load().ple_prefetch(ctypes.byref(L), ctypes.byref(b), _ptr(staging), _stream(stream)),
                "ple_prefetch")
     return staging
@@ -198,16 +281,25 @@ def ple_prefetch_dedup(layer: Layer, input_ids, query_start_loc, staging, *, wor
                        ngram_context=None, ngram_context_out=None, stream=None):
     """ple_prefetch reading each distinct table row once; num_unique (device int32 [1]) receives
     the number of distinct rows."""
+    _req("input_ids", input_ids, (None,), _I32)
     T = input_ids.shape[0]
+    _req("staging", staging, (T, layer.hash.num_heads * layer.table.dim), _BF16)
+    _req("num_unique", num_unique, (1,), _I32, optional=True)
     need = ple_prefetch_dedup_workspace_bytes(T, layer.hash.num_heads)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=input_ids.device)
+    _req_bytes("workspace", workspace, need)
     L = layer.desc()
-    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out)
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, context_len=layer.hash.context_len)
+    _same_device(input_ids, staging, num_unique, workspace)
     capi.check(capi.load().ple_prefetch_dedup(ctypes.byref(L), ctypes.byref(b), _ptr(staging), _ptr(workspace),
-                                              workspace.numel(), _ptr(num_unique), _stream(stream)),
+                                              _nbytes(workspace), _ptr(num_unique), _stream(stream)),
                "ple_prefetch_dedup")
     return staging
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size() if isinstance(t, torch.Tensor) else (1 << 62)
 
 
 def ple_dp_gather_slot(token_counts, group_size: int, dp_rank: int) -> tuple[int, int]:
@@ -229,40 +321,60 @@ def ple_head_shard(num_heads: int, tp_size: int, tp_rank: int, dp_size: int, dp_
 
 def ple_select_rows(gathered, rank: int, num_tokens: int, *, out=None, stream=None):
     """gathered bf16 [E][E*slot][W] -> out bf16 [num_tokens][E*W] (rank's token window, shards in order)."""
+    _req("gathered", gathered, (None, None, None), _BF16)
     E, rows, W = gathered.shape
+    if E < 1 or rows % E != 0:
+        raise ValueError(f"gathered has {rows} rows per shard, not a multiple of its {E} shards")
     slot = rows // E
     if out is None:
         out = torch.empty((num_tokens, E * W), dtype=torch.bfloat16, device=gathered.device)
+    _req("out", out, (num_tokens, E * W), _BF16)
+    _same_device(gathered, out)
     capi.check(capi.load().ple_select_rows(_ptr(gathered), E, slot, rank, num_tokens, W, _ptr(out),
                                            _stream(stream)), "ple_select_rows")
     return out
 
 
 def ple_kv_proj(x, w, *, kv=None, stream=None):
+    _req("x", x, (None, None), _BF16)
     T, K = x.shape
+    _req("w", w, (None, K), _BF16)
     O = w.shape[0]
     if kv is None:
         kv = torch.empty((T, O), dtype=torch.bfloat16, device=x.device)
+    _req("kv", kv, (T, O), _BF16)
+    _same_device(x, w, kv)
     capi.check(capi.load().ple_kv_proj(_ptr(x), _ptr(w), T, K, O, _ptr(kv), _stream(stream)), "ple_kv_proj")
     return kv
 
 
 def ple_gate(hidden, kv, *, eps: float = 1e-6, out=None, gate=None, want_gate: bool = True, stream=None):
+    _req("hidden", hidden, (None, None), _BF16)
     T, N = hidden.shape
+    _req("kv", kv, (T, 2 * N), _BF16)
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=hidden.device)
     if gate is None and want_gate:
         gate = torch.empty((T,), dtype=torch.float32, device=hidden.device)
+    _req("out", out, (T, N), _BF16)
+    _req("gate", gate, (T,), _F32, optional=True)
+    _same_device(hidden, kv, out, gate)
     capi.check(capi.load().ple_gate(_ptr(hidden), _ptr(kv), T, N, eps, _ptr(out), _ptr(gate), _stream(stream)),
                "ple_gate")
     return out, gate
 
 
 def ple_conv(x, query_start_loc, w, *, dilation: int, conv_state=None, conv_state_out=None, y=None, stream=None):
+    _req("x", x, (None, None), _BF16)
     T, N = x.shape
+    _req("w", w, (N, None), _BF16)
+    S = (int(w.shape[1]) - 1) * int(dilation)
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
-    b = _batch(None, query_start_loc, conv_state=conv_state, conv_state_out=conv_state_out, num_tokens=T)
+    _req("y", y, (T, N), _BF16)
+    b = _batch(None, query_start_loc, conv_state=conv_state, conv_state_out=conv_state_out, num_tokens=T,
+               state_shape=(S, N))
+    _same_device(x, w, y, query_start_loc)
     capi.check(capi.load().ple_conv(_ptr(x), ctypes.byref(b), _ptr(w), N, w.shape[1], dilation, _ptr(y),
                                     _stream(stream)), "ple_conv")
     return y
@@ -272,9 +384,19 @@ def ple_spec_commit(input_ids, query_start_loc, accepted, *, hash: HashParams = 
                     ngram_context_out=None, x=None, conv_kernel: int = 1, conv_dilation: int = 1, conv_state=None,
                     conv_state_out=None, stream=None):
     """State after a speculative verify step that keeps accepted[r] tokens of request r."""
+    if x is not None:
+        _req("x", x, (None, None), _BF16)
     N = int(x.shape[1]) if x is not None else (int(conv_state_out.shape[2]) if conv_state_out is not None else 0)
+    S = (int(conv_kernel) - 1) * int(conv_dilation)
+    R = int(query_start_loc.shape[0]) - 1
+    _req("accepted", accepted, (R,), _I32)
+    T = int(input_ids.shape[0]) if input_ids is not None else (x.shape[0] if x is not None else 0)
+    if x is not None:
+        _req("x", x, (T, N), _BF16)
     b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out,
-               num_tokens=None if input_ids is not None else (x.shape[0] if x is not None else 0))
+               num_tokens=None if input_ids is not None else T,
+               context_len=hash.context_len if hash is not None else None, state_shape=(S, N))
+    _same_device(input_ids, query_start_loc, accepted, x)
     h = hash.desc() if hash is not None else None
     capi.check(capi.load().ple_spec_commit(ctypes.byref(h) if h is not None else None, ctypes.byref(b),
                                            _ptr(accepted), _ptr(x), N, conv_kernel, conv_dilation, _stream(stream)),
@@ -295,23 +417,41 @@ def prefill_conv_input(layer: Layer, workspace, num_tokens: int):
     return workspace[off:off + T * N * 2].view(torch.bfloat16).view(T, N)
 
 
+def prefill_kv(layer: Layer, workspace, num_tokens: int):
+    """View of kv_proj's output (bf16 [T][2N]: key, then value) a ple_prefill_fused call leaves in its
+    workspace."""
+    def r256(n):
+        return (n + 255) // 256 * 256
+    T, N = int(num_tokens), layer.hidden
+    off = r256(T * layer.hash.num_heads * layer.table.dim * 2)
+    return workspace[off:off + T * 2 * N * 2].view(torch.bfloat16).view(T, 2 * N)
+
+
 def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefetched_rows=None, ngram_context=None,
                       ngram_context_out=None, conv_state=None, conv_state_out=None, out=None, gate=None,
                       workspace=None, max_request_tokens=0, stream=None):
     """max_request_tokens: 0 (unknown) or 1..4 (no request has more tokens: a decode step or
     speculative verify windows, run with one kernel for gate, conv and the carried state and
     context)."""
+    _req("hidden", hidden, (None, layer.hidden), _BF16)
     T, N = hidden.shape
+    _req("input_ids", input_ids, (T,), _I32)
+    _req("prefetched_rows", prefetched_rows, (T, layer.hash.num_heads * layer.table.dim), _BF16, optional=True)
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=hidden.device)
+    _req("out", out, (T, N), _BF16)
+    _req("gate", gate, (T,), _F32, optional=True)
     need = ple_prefill_workspace_bytes(layer, T)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=hidden.device)
+    _req_bytes("workspace", workspace, need)
     L = layer.desc()
+    S = (layer.conv_kernel - 1) * layer.conv_dilation
     b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out,
-               max_request_tokens=max_request_tokens)
+               max_request_tokens=max_request_tokens, context_len=layer.hash.context_len, state_shape=(S, N))
+    _same_device(input_ids, hidden, prefetched_rows, out, gate, workspace, layer.kv_weight, layer.conv_weight)
     capi.check(capi.load().ple_prefill_fused(ctypes.byref(L), ctypes.byref(b), _ptr(hidden), _ptr(prefetched_rows),
-                                             _ptr(out), _ptr(gate), _ptr(workspace), workspace.numel(),
+                                             _ptr(out), _ptr(gate), _ptr(workspace), _nbytes(workspace),
                                              _stream(stream)), "ple_prefill_fused")
     return out
 

@@ -603,12 +603,15 @@ size_t ple_prefill_workspace_bytes(const ple_layer_desc* layer, int64_t max_toke
     return round256(T * HD * 2) + round256(T * 2 * N * 2) + round256(T * N * 2);
 }
 
-int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
-                      const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-    HashParams hp;
-    int cpr_log2 = -1;
-    int rc = validate_layer(layer, &hp, &cpr_log2);
+}  // extern "C"
+
+namespace {
+
+// Checks of a fused prefill call apart from its workspace.
+int prefill_checks(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
+                   const uint16_t* prefetched_rows, const uint16_t* out, const float* gate, HashParams* hp,
+                   int* cpr_log2) {
+    int rc = validate_layer(layer, hp, cpr_log2);
     if (rc) return rc;
     rc = validate_batch_tokens(batch);
     if (rc) return rc;
@@ -630,22 +633,27 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
         if (hidden == nullptr || out == nullptr || !aligned16(hidden) || !aligned16(out))
             return fail(PLE_ERR_INVALID_ARGUMENT, "hidden and out must be non-NULL and 16-byte aligned");
         if (gate != nullptr && !aligned4(gate)) return fail(PLE_ERR_INVALID_ARGUMENT, "gate output is misaligned");
-        if (workspace == nullptr) return fail(PLE_ERR_WORKSPACE, "workspace is NULL");
-        const size_t need = ple_prefill_workspace_bytes(layer, T);
-        if (workspace_bytes < need)
-            return fail(PLE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
-                        workspace_bytes, need);
-        if (((uintptr_t)workspace & 255u) != 0)
-            return fail(PLE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
     }
+    return PLE_OK;
+}
+
+// Whether a checked fused prefill call has any work (T == 0 still carries
+// the state and context).
+bool prefill_has_work(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* prefetched_rows) {
     const bool state_work = batch->conv_state_out != nullptr && batch->num_reqs > 0 && layer->conv_kernel > 1;
     const bool ctx_work = prefetched_rows == nullptr && batch->ngram_context_out != nullptr && batch->num_reqs > 0;
-    if (T == 0 && !state_work && !ctx_work) return ok();
-    rc = check_device();
-    if (rc) return rc;
-    hipStream_t s = (hipStream_t)stream;
+    return batch->num_tokens > 0 || state_work || ctx_work;
+}
 
-    char* ws = (char*)workspace;
+// The launches of a checked fused prefill call, with its intermediates in ws.
+int prefill_run(const ple_layer_desc* layer, const ple_batch_desc* batch, const HashParams& hp, int cpr_log2,
+                const uint16_t* hidden, const uint16_t* prefetched_rows, uint16_t* out, float* gate, char* ws,
+                hipStream_t s) {
+    const int N = layer->hidden;
+    const int HD = layer->hash.num_heads * layer->table.dim;
+    const int64_t T = batch->num_tokens;
+    const bool state_work = batch->conv_state_out != nullptr && batch->num_reqs > 0 && layer->conv_kernel > 1;
+    const bool ctx_work = prefetched_rows == nullptr && batch->ngram_context_out != nullptr && batch->num_reqs > 0;
     uint16_t* rows = (uint16_t*)ws;
     uint16_t* kv = (uint16_t*)(ws + round256((size_t)T * HD * 2));
     uint16_t* gated = (uint16_t*)((char*)kv + round256((size_t)T * 2 * N * 2));
@@ -686,7 +694,7 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
         a.gate = gate;
         e = launch_decode_tail(a, layer->conv_kernel, s);
         if (e != hipSuccess) return hip_fail(e, "decode tail launch");
-        return ok();
+        return PLE_OK;
     }
     if (T > 0) {
         e = launch_gate(hidden, kv, T, N, layer->eps, gated, gate, s);
@@ -707,7 +715,36 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
                                layer->hash.eos_token_id, ctx_work ? batch->ngram_context_out : nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "state launch");
     }
-    return ok();
+    return PLE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
+                      const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    HashParams hp;
+    int cpr_log2 = -1;
+    int rc = prefill_checks(layer, batch, hidden, prefetched_rows, out, gate, &hp, &cpr_log2);
+    if (rc) return rc;
+    const int64_t T = batch->num_tokens;
+    if (T > 0) {
+        if (workspace == nullptr) return fail(PLE_ERR_WORKSPACE, "workspace is NULL");
+        const size_t need = ple_prefill_workspace_bytes(layer, T);
+        if (workspace_bytes < need)
+            return fail(PLE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                        workspace_bytes, need);
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(PLE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    }
+    if (!prefill_has_work(layer, batch, prefetched_rows)) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    rc = prefill_run(layer, batch, hp, cpr_log2, hidden, prefetched_rows, out, gate, (char*)workspace,
+                     (hipStream_t)stream);
+    return rc ? rc : ok();
 }
 
 int ple_host_alloc(size_t bytes, void** host, void** device) {

@@ -235,102 +235,6 @@ __global__ __launch_bounds__(256) void conv_kernel(const uint16_t* __restrict__ 
     }
 }
 
-// Tiled convolution for compile-time kernel sizes.  A block covers TB
-// consecutive tokens x 256 chunks of 8 channels.  Wave 0 finds the request of
-// each of the TB tokens with one cooperative load of query_start_loc and puts
-// (request, start) in LDS; then every lane walks its channel chunk through the
-// TB tokens, TT tokens at a time, issuing all TT x KC tap loads before using
-// any (16 loads in flight per lane for KC = 4).  Rows re-read by neighbouring
-// tokens hit L2, so HBM sees each input row about once.
-template <int KC, int TB, int TT>
-__global__ __launch_bounds__(256) void conv_tile_kernel(const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ qsl, int64_t T, int R,
-                                                        const uint16_t* __restrict__ state,
-                                                        const uint16_t* __restrict__ w, int N, int d,
-                                                        uint16_t* __restrict__ y) {
-    __shared__ int32_t s_r[TB];
-    __shared__ int64_t s_a[TB];
-    const int tid = threadIdx.x;
-    const int nch = N >> 3;
-    const int64_t t0 = (int64_t)blockIdx.x * TB;
-    const int nt = (int)min((int64_t)TB, T - t0);
-    const int64_t S = (int64_t)(KC - 1) * d;
-    if (tid < kWave) {
-        const int my_k = tid < nt ? tid : 0;
-        int r;
-        int64_t a;
-        wave_find_request(qsl, R, t0 + my_k, t0, nt, my_k, tid, r, a);
-        if (tid < nt) {
-            s_r[tid] = r;
-            s_a[tid] = a;
-        }
-    }
-    __syncthreads();
-
-    const int c = blockIdx.y * 256 + tid;
-    if (c >= nch) return;  // no barrier below
-    const int c0 = c * 8;
-    float wt[8][KC];
-    {
-        const u32x4* wp = (const u32x4*)(w + (int64_t)c0 * KC);
-        uint32_t words[4 * KC];
-#pragma unroll
-        for (int q = 0; q < KC; ++q) {
-            const u32x4 v4 = wp[q];
-            words[4 * q] = v4.x; words[4 * q + 1] = v4.y; words[4 * q + 2] = v4.z; words[4 * q + 3] = v4.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int k = 0; k < KC; ++k) {
-                const int flat = e * KC + k;
-                wt[e][k] = (flat & 1) ? bf16_hi(words[flat >> 1]) : bf16_lo(words[flat >> 1]);
-            }
-    }
-
-    for (int k0 = 0; k0 < nt; k0 += TT) {
-        u32x4 xv[TT][KC];
-#pragma unroll
-        for (int kk = 0; kk < TT; ++kk) {
-            const int k = k0 + kk;
-            const bool valid = k < nt;
-            const int kc = valid ? k : 0;
-            const int64_t t = t0 + kc;
-            const int64_t a = s_a[kc];
-            const int r = s_r[kc];
-#pragma unroll
-            for (int i = 0; i < KC; ++i) {
-                const int64_t p = t - (int64_t)i * d;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (valid) {
-                    if (p >= a)
-                        v = *(const u32x4*)(x + p * N + c0);
-                    else if (state != nullptr)
-                        v = *(const u32x4*)(state + ((int64_t)r * S + (S - (a - p))) * N + c0);
-                }
-                xv[kk][i] = v;
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < TT; ++kk) {
-            const int k = k0 + kk;
-            if (k < nt) {
-                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < KC; ++i) {
-                    float f[8];
-                    unpack8(xv[kk][i], f);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] += wt[e][KC - 1 - i] * f[e];
-                }
-                *(u32x4*)(y + (t0 + k) * N + c0) =
-                    u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                          pack_bf16x2(acc[6], acc[7])};
-            }
-        }
-    }
-}
-
 // LDS-staged convolution.  A block covers TB consecutive tokens x 64 chunks of
 // 8 channels (1 KiB of each row).  It stages the rows [t0 - S, t0 + TB) of its
 // channel slice in LDS once (every input element is read from HBM once, plus
@@ -608,45 +512,13 @@ __global__ __launch_bounds__(512) void decode_tail_kernel(DecodeTailArgs a) {
     const int n = (int)min(tb - ta, (int64_t)(1 << 30));
     const int N = a.N, nch = N >> 3;
     const int S = (KC - 1) * a.d;
+    const bool token_wave = wid < kTailTokens;  // wave-uniform
 
-    if (wid >= kTailTokens) {  // waves 4-7: carried state shift (a quarter each) and context
-        const int cw = wid - kTailTokens;
-        if (cw == 0 && a.ctx_out != nullptr && lane < a.C)
-            a.ctx_out[(int64_t)r * a.C + lane] = carried_token(a.tok, a.ctx, a.C, a.eos, r, lane, ta, tb);
-        if (a.state_out != nullptr && S > n) {
-            // out rows m < S - n take old rows m + n (zeros without a state):
-            // a flat copy of (S - n) * nch chunks, 16 in flight per lane
-            constexpr int U = 16;
-            const int all = (S - n) * nch;
-            const int per = (all + 4 * kWave - 1) / (4 * kWave) * kWave;  // whole passes of 64 chunks
-            const int lo = cw * per;
-            const int total = min(all, lo + per);
-            const u32x4* src = a.state != nullptr ? (const u32x4*)(a.state + ((int64_t)r * S + n) * N) : nullptr;
-            u32x4* dst = (u32x4*)(a.state_out + (int64_t)r * S * N);
-            for (int base = lo; base < total; base += U * kWave) {
-                u32x4 vv[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int idx = base + u * kWave + lane;
-                    vv[u] = (src != nullptr && idx < total) ? src[idx] : u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int idx = base + u * kWave + lane;
-                    if (idx < total) dst[idx] = vv[u];
-                }
-            }
-        }
-        __syncthreads();  // every wave of the block meets the token waves' barrier
-        return;
-    }
-
-    const int j = wid;  // token slot
-    const bool has = j < n;
+    // token wave j: slot j of the window
+    const int j = token_wave ? wid : 0;
+    const bool has = token_wave && j < n;
     const int64_t t = has ? ta + j : 0;
-    const u32x4* __restrict__ h = (const u32x4*)(a.hidden + t * N);
-    const u32x4* __restrict__ k = (const u32x4*)(a.kv + t * 2 * (int64_t)N);
-    const u32x4* __restrict__ v = k + nch;
+    const u32x4* __restrict__ v = (const u32x4*)(a.kv + t * 2 * (int64_t)N) + nch;
     const u32x4* __restrict__ wc = (const u32x4*)a.conv_w;  // chunk c's weights: KC chunks from c*KC
     // tap i (1..KC-1) of this token: inside the window (slot j - i*d of the
     // block's LDS) or before it (carried state row S - (i*d - j), or zero)
@@ -672,50 +544,88 @@ __global__ __launch_bounds__(512) void decode_tail_kernel(DecodeTailArgs a) {
         }
     };
     const bool one_pass = nch <= G * kWave;
-    if (one_pass) load_pass(0);  // independent of the gate: in flight with h and k
 
-    // per-lane partial sums in gate_kernel's order (chunks lane, lane+64, ...)
-    constexpr int UNROLL = 8;
-    float hh = 0.f, kk = 0.f, hk = 0.f;
-    if (has) {
-        for (int base = lane; base < nch; base += 64 * UNROLL) {
-            u32x4 hv[UNROLL], kv4[UNROLL];
+    if (!token_wave) {
+        // waves 4-7: carried state shift (a quarter each) and context
+        const int cw = wid - kTailTokens;
+        if (cw == 0 && a.ctx_out != nullptr && lane < a.C)
+            a.ctx_out[(int64_t)r * a.C + lane] = carried_token(a.tok, a.ctx, a.C, a.eos, r, lane, ta, tb);
+        if (a.state_out != nullptr && S > n) {
+            // out rows m < S - n take old rows m + n (zeros without a state):
+            // a flat copy of (S - n) * nch chunks, 16 in flight per lane
+            constexpr int U = 16;
+            const int all = (S - n) * nch;
+            const int per = (all + 4 * kWave - 1) / (4 * kWave) * kWave;  // whole passes of 64 chunks
+            const int lo = cw * per;
+            const int total = min(all, lo + per);
+            const u32x4* src = a.state != nullptr ? (const u32x4*)(a.state + ((int64_t)r * S + n) * N) : nullptr;
+            u32x4* dst = (u32x4*)(a.state_out + (int64_t)r * S * N);
+            for (int base = lo; base < total; base += U * kWave) {
+                u32x4 cp[U];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int idx = base + 64 * u;
-                if (idx < nch) {
-                    hv[u] = h[idx];
-                    kv4[u] = k[idx];
+                for (int u = 0; u < U; ++u) {
+                    const int idx = base + u * kWave + lane;
+                    cp[u] = (src != nullptr && idx < total) ? src[idx] : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = base + u * kWave + lane;
+                    if (idx < total) dst[idx] = cp[u];
                 }
             }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                if (base + 64 * u < nch) acc_dot(hv[u], kv4[u], hh, kk, hk);
         }
-    }
-    const float g = token_gate(hh, kk, hk, N, a.eps);
-    if (has && lane == 0 && a.gate != nullptr) a.gate[t] = g;
-    // the newest carried state rows are the window's last S gated rows
-    const int srow = j + S - n;
-    uint16_t* st_row = (has && a.state_out != nullptr && srow >= 0 && srow < S)
-                           ? a.state_out + ((int64_t)r * S + srow) * N
-                           : nullptr;
+    } else {
+        const u32x4* __restrict__ h = (const u32x4*)(a.hidden + t * N);
+        const u32x4* __restrict__ k = (const u32x4*)(a.kv + t * 2 * (int64_t)N);
+        if (one_pass) load_pass(0);  // independent of the gate: in flight with h and k
 
-    // gated rows: to memory, LDS and the carried state
-    for (int c0 = 0; c0 < nch; c0 += G * kWave) {
-        if (!one_pass) load_pass(c0);
+        // per-lane partial sums in gate_kernel's order (chunks lane, lane+64, ...)
+        constexpr int UNROLL = 8;
+        float hh = 0.f, kk = 0.f, hk = 0.f;
+        if (has) {
+            for (int base = lane; base < nch; base += 64 * UNROLL) {
+                u32x4 hv[UNROLL], kv4[UNROLL];
 #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int c = c0 + q * kWave + lane;
-            if (has && c < nch) {
-                const u32x4 gv = gate_chunk(g, vv[q]);
-                s_gated[j * nch + c] = gv;
-                ((u32x4*)(a.gated + t * N))[c] = gv;
-                if (st_row != nullptr) ((u32x4*)st_row)[c] = gv;
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int idx = base + 64 * u;
+                    if (idx < nch) {
+                        hv[u] = h[idx];
+                        kv4[u] = k[idx];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (base + 64 * u < nch) acc_dot(hv[u], kv4[u], hh, kk, hk);
+            }
+        }
+        const float g = token_gate(hh, kk, hk, N, a.eps);
+        if (has && lane == 0 && a.gate != nullptr) a.gate[t] = g;
+        // the newest carried state rows are the window's last S gated rows
+        const int srow = j + S - n;
+        uint16_t* st_row = (has && a.state_out != nullptr && srow >= 0 && srow < S)
+                               ? a.state_out + ((int64_t)r * S + srow) * N
+                               : nullptr;
+
+        // gated rows: to memory, LDS and the carried state
+        for (int c0 = 0; c0 < nch; c0 += G * kWave) {
+            if (!one_pass) load_pass(c0);
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                const int c = c0 + q * kWave + lane;
+                if (has && c < nch) {
+                    const u32x4 gv = gate_chunk(g, vv[q]);
+                    s_gated[j * nch + c] = gv;
+                    ((u32x4*)(a.gated + t * N))[c] = gv;
+                    if (st_row != nullptr) ((u32x4*)st_row)[c] = gv;
+                }
             }
         }
     }
+    // the one barrier of the block: every wave reaches it, the token waves'
+    // gated rows are then in LDS
     __syncthreads();
+    if (!token_wave) return;
+
     // conv: tap 0 is this token, taps inside the window from LDS
     for (int c0 = 0; c0 < nch; c0 += G * kWave) {
         if (!one_pass) load_pass(c0);

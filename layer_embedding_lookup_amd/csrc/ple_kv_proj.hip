@@ -10,7 +10,7 @@
 // eight waves of 128 x 64 with 16x16x32 MFMAs (kv_proj_pipe8w, two waves per
 // SIMD); smaller ones on one four-wave pipelined body of 32x32x16 MFMAs at
 // 128 x 128 tiles (a 1024-token speculative-verify batch) or 64 x 64 tiles
-// (decode batches), which PLE_KV_WIDE=0 also uses for the 256-wide tiles.
+// (decode batches).
 // The designs are described above the bodies.  The block tile is the largest
 // that still gives 256 blocks, one per CU.  Blocks are numbered so that the blocks resident on one XCD (block id
 // mod 8 picks the XCD) work on neighbouring tiles and share their x and W
@@ -41,18 +41,15 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel body: BT x BT block tile, 4 waves (one per SIMD), each a
-// (BT/2) x (BT/2) block held in accumulator tiles of 32 x 32.  For BT = 256
-// that is 16 tiles (256 registers per lane, in the accumulation half of the
-// register file) and two LDS stages of 64 KiB; for BT = 128, 4 tiles and
-// stages of 32 KiB; for BT = 64, one tile and stages of 16 KiB.  K-slices
-// of 64.
+// Pipelined kernel body for batches too small to give 256 blocks of 256 x
+// 256: BT x BT block tile, 4 waves (one per SIMD), each a (BT/2) x (BT/2)
+// block held in accumulator tiles of 32 x 32.  For BT = 128 that is 4 tiles
+// and LDS stages of 32 KiB; for BT = 64, one tile and stages of 16 KiB.
+// K-slices of 64.
 //
-// Why this shape: a wave's LDS traffic per MFMA falls as its block grows,
-// and 128 x 128 is the largest block whose accumulators fit one wave; the
-// fragment reads of the next 16-deep K-step are spread between the current
-// step's MFMAs, so with one wave per SIMD the matrix core stays fed without
-// a second wave to cover for it.  The narrower tiles trade that for
+// Why this shape: the fragment reads of the next 16-deep K-step are spread
+// between the current step's MFMAs, so with one wave per SIMD the matrix core
+// stays fed without a second wave to cover for it; the narrow tiles give
 // blocks: a 1024-token batch gets 256 blocks of 128 x 128, a 256-token decode
 // batch 256 blocks of 64 x 64 (there the W panels, read by four blocks each
 // from the XCD's L2, bound the kernel, not the matrix cores).
@@ -85,9 +82,6 @@ constexpr int kBigThreads = 256;
 constexpr int kBBK = 64;
 constexpr int kNStage = 2;
 constexpr int kBigMaxK = 1 << 20;  // keeps 256 rows of K bf16 within a 32-bit buffer offset
-#ifndef PLE_KV_WIDE
-#define PLE_KV_WIDE 1  // 256-wide tiles: eight waves of 128 x 64 on 16x16x32 MFMAs
-#endif
 
 // Block tile BT x BT (256, or 128 / 64 for problems too small to fill the
 // chip with wider tiles); each of the 4 waves holds a (BT/2) x (BT/2) block
@@ -513,13 +507,8 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
 #undef PLE_FRAG_REGS2
 #undef PLE_FRAG_REGS1
 
-// The two block tiles as plain kernels (their bodies use device-only
+// The block tiles as plain kernels (their bodies use device-only
 // builtins, which a kernel template would also instantiate for the host).
-__global__ __launch_bounds__(kBigThreads, 1) void kv_proj_big_kernel(const uint16_t* __restrict__ x,
-                                                                     const uint16_t* __restrict__ w, int M, int K,
-                                                                     int O, uint16_t* __restrict__ out) {
-    kv_proj_pipe<256>(x, w, M, K, O, out);
-}
 __global__ __launch_bounds__(kWideThreads, 1) void kv_proj_wide_kernel(const uint16_t* __restrict__ x,
                                                                        const uint16_t* __restrict__ w, int M, int K,
                                                                        int O, uint16_t* __restrict__ out) {
@@ -540,16 +529,12 @@ template <int BT>
 static hipError_t launch_kv_proj_pipe(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                                       hipStream_t s) {
     using P = PipeShape<BT>;
-    const void* fn = BT == 256   ? (const void*)kv_proj_big_kernel
-                     : BT == 128 ? (const void*)kv_proj_mid_kernel
-                                 : (const void*)kv_proj_small_kernel;
+    static_assert(BT == 128 || BT == 64, "256-wide tiles run on the eight-wave body");
+    const void* fn = BT == 128 ? (const void*)kv_proj_mid_kernel : (const void*)kv_proj_small_kernel;
     static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = (int)((M + BT - 1) / BT) * ((O + BT - 1) / BT);
-    if (BT == 256)
-        hipLaunchKernelGGL(kv_proj_big_kernel, dim3(tiles), dim3(kBigThreads), P::LDS_BYTES, s, x, w, (int)M, K, O,
-                           kv);
-    else if (BT == 128)
+    if (BT == 128)
         hipLaunchKernelGGL(kv_proj_mid_kernel, dim3(tiles), dim3(kBigThreads), P::LDS_BYTES, s, x, w, (int)M, K, O,
                            kv);
     else
@@ -563,7 +548,7 @@ hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K
     // the widest block tile that still gives 256 blocks
     if (K > kBigMaxK) return hipErrorInvalidValue;  // rejected by the argument checks before this
     const int64_t big_tiles = ((M + 255) / 256) * ((O + 255) / 256);
-    if (PLE_KV_WIDE && big_tiles >= 256) {
+    if (big_tiles >= 256) {
         using P = PipeShape<256>;
         static const hipError_t attr = hipFuncSetAttribute((const void*)kv_proj_wide_kernel,
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS_BYTES);
@@ -572,7 +557,6 @@ hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K
                            (int)M, K, O, kv);
         return hipGetLastError();
     }
-    if (big_tiles >= 256) return launch_kv_proj_pipe<256>(x, w, M, K, O, kv, s);
     // (64-wide tiles take 128 KiB of LDS, so only while one block per CU covers them)
     const int64_t mid_tiles = ((M + 127) / 128) * ((O + 127) / 128);
     const int64_t small_tiles = ((M + 63) / 64) * ((O + 63) / 64);

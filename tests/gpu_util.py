@@ -60,3 +60,75 @@ def oracle_ids(batch: wl.Batch, layer: int = 0, first_head: int = 0, num_heads: 
                             batch.offsets[sl], context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram,
                             eos_token_id=wl.EOS, ngram_context=batch.ngram_context, first_head=first_head,
                             num_heads=H, want_context_out=want_context_out)
+
+
+def oracle_threads() -> int:
+    """Worker threads for the oracle's per-token work: the host's CPU share, at most 16."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_kv_proj_threaded(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """oracle.kv_proj on blocks of rows in parallel threads.  Each output row is
+    the oracle's own computation on that row (the C call releases the GIL); the
+    split only spreads independent rows over the host cores."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    T = x.shape[0]
+    out = np.empty((T, w.shape[0]), dtype=np.uint16)
+    if T == 0:
+        return out
+    n = oracle_threads()
+    bounds = np.linspace(0, T, min(T, n) + 1).astype(np.int64)  # one block per thread: each call widens W once
+
+    def one(i):
+        lo, hi = int(bounds[i]), int(bounds[i + 1])
+        if hi > lo:
+            out[lo:hi] = oracle.kv_proj(np.ascontiguousarray(x[lo:hi]), w)
+
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(one, range(len(bounds) - 1)))
+    return out
+
+
+GATE_REL_TOL = 1e-5
+BF16_ABS_TOL = 2e-2
+
+
+def check_gate_conv_stages(hidden, kv_gpu, gate_gpu, gated_gpu, y_gpu, qsl, conv_w, dilation, eps, *,
+                           conv_state=None, state_out_gpu=None, tokens=None):
+    """Stage-wise parity of the gate and the conv: each compared with the oracle
+    run on the GPU's own input to that stage (its kv, its conv input), so the
+    fp32 gate is held to rel 1e-5 and the bf16 outputs to one ulp and max-abs
+    2e-2, and the carried conv state is a bit-exact copy.  `tokens` restricts
+    the comparison to those tokens (every token when None)."""
+    import oracle
+    T = hidden.shape[0]
+    if T == 0:
+        return
+    sel = np.arange(T) if tokens is None else np.asarray(tokens)
+    want_gated, g_want = oracle.gate(hidden[sel], kv_gpu[sel], eps)
+    if gate_gpu is not None:
+        np.testing.assert_allclose(np.asarray(gate_gpu, np.float64)[sel], g_want, rtol=GATE_REL_TOL, atol=0)
+    assert np.abs(bf16_f64(gated_gpu[sel]) - bf16_f64(want_gated)).max() <= BF16_ABS_TOL
+    assert bf16_ulp_distance(gated_gpu[sel], want_gated).max() <= 1
+    y_want, st_want = oracle.conv(gated_gpu, qsl, conv_w, dilation, state=conv_state, want_state_out=True)
+    assert np.abs(bf16_f64(y_gpu[sel]) - bf16_f64(y_want[sel])).max() <= BF16_ABS_TOL
+    # fp32 sum of Kc exact bf16 products: |error| <= gamma_Kc * sum |w x|, plus one bf16 ulp of the
+    # result (both sides round to bf16); away from cancellation that is one ulp
+    Kc = conv_w.shape[1]
+    gamma = Kc * 2.0 ** -24 / (1 - Kc * 2.0 ** -24)
+    mag = oracle.conv(gated_gpu & np.uint16(0x7FFF), qsl, conv_w & np.uint16(0x7FFF), dilation,
+                      state=None if conv_state is None else conv_state & np.uint16(0x7FFF))
+    e = bf16_f64(y_want[sel])
+    ulp = np.maximum(np.abs(e), 2.0 ** -126) * 2.0 ** -7
+    assert (np.abs(bf16_f64(y_gpu[sel]) - e) <= gamma * bf16_f64(mag[sel]) * 1.01 + ulp).all()
+    d = bf16_ulp_distance(y_gpu[sel], y_want[sel])
+    assert d[np.abs(e) > 1e-2].max(initial=0) <= 1
+    if state_out_gpu is not None:
+        np.testing.assert_array_equal(state_out_gpu, st_want)

@@ -14,8 +14,8 @@ import torch
 import layer_embedding_lookup_amd as ple
 import oracle
 import workloads as wl
-from gpu_util import (DEV, bf16_f64, bf16_ulp_distance, dev, dev_bf16, hash_params, host_bits, log,
-                      oracle_ids)
+from gpu_util import (DEV, bf16_f64, bf16_ulp_distance, check_gate_conv_stages, dev, dev_bf16, hash_params,
+                      host_bits, log, oracle_ids)
 
 pytestmark = pytest.mark.gpu
 
@@ -380,8 +380,14 @@ CONV_CASES = [
     ([1] * 64, 2048, 4, 3, True),
     ([0, 5, 0, 0, 40, 1, 0], 64, 3, 5, True),
     ([50, 20], 64, 1, 1, False),
-    ([33, 0, 9], 72, 7, 2, True),   # generic kernel size path
+    ([33, 0, 9], 72, 7, 2, True),   # kernel size 7: the LDS-staged tile kernel
     ([100], 16, 2, 9, True),
+    # the generic kernel (any kernel size, any span): kernel sizes above 8,
+    # spans above 64 rows, and weights wider than 64 KiB with a span above 64
+    ([30, 0, 17, 1], 16, 12, 2, True),
+    ([25, 3, 0, 40], 24, 6, 13, True),
+    ([9, 70, 1], 8200, 4, 22, True),
+    ([5, 90], 64, 16, 1, False),
 ]
 
 
@@ -443,6 +449,9 @@ def _oracle_chain(cfg, b, table, scales, kvw, cw, hidden, tokens=None, layer=0):
 
 @pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2"])
 def test_prefill_fused_parity_small(variant):
+    """The whole chain against the oracle's chain (out within 2e-2), and each stage against the oracle
+    run on the GPU's own input to it: kv_proj on the gathered rows, the fp32 gate at rel 1e-5 on the
+    GPU's kv (read from the workspace), the conv on the GPU's conv input."""
     cfg = wl.CONFIGS[2 if variant == "cfg2" else 1]
     if variant == "cfg1-ctx-state":
         b = wl.make_batch(cfg, with_context=True, with_state=True)
@@ -456,20 +465,21 @@ def test_prefill_fused_parity_small(variant):
     st_out = torch.empty((b.R, S, cfg.N), dtype=torch.bfloat16, device=DEV)
     ctx_out = torch.empty((b.R, cfg.context_len), dtype=torch.int32, device=DEV)
     gate = torch.empty((cfg.T,), dtype=torch.float32, device=DEV)
+    ws = torch.empty((ple.ple_prefill_workspace_bytes(L, cfg.T),), dtype=torch.uint8, device=DEV)
     out = ple.ple_prefill_fused(L, dev(b.input_ids), dev(b.qsl), dev_bf16(hidden),
                                 ngram_context=None if b.ngram_context is None else dev(b.ngram_context),
                                 ngram_context_out=ctx_out,
                                 conv_state=None if b.conv_state is None else dev_bf16(b.conv_state),
-                                conv_state_out=st_out, gate=gate)
+                                conv_state_out=st_out, gate=gate, workspace=ws)
     got = host_bits(out)
     assert np.abs(bf16_f64(got) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
-    # the gate sees kv rounded to bf16 on both sides, which may differ by one ulp: compare loosely
-    np.testing.assert_allclose(gate.cpu().numpy(), ref["gate"], rtol=5e-3)
     _, want_ctx = oracle_ids(b, want_context_out=True)
     np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
-    _, st_ref = oracle.conv(ref["gated"], b.qsl, cw, cfg.conv_dilation, state=b.conv_state, want_state_out=True)
-    # the carried state holds gated values (bf16 outputs of the gate)
-    assert np.abs(bf16_f64(host_bits(st_out)) - bf16_f64(st_ref)).max() <= GATE_ABS_TOL
+    kv_gpu = host_bits(ple.prefill_kv(L, ws, cfg.T))
+    _check_kv(kv_gpu, ref["kv"], ref["rows"], kvw)
+    check_gate_conv_stages(hidden, kv_gpu, gate.cpu().numpy(), host_bits(ple.prefill_conv_input(L, ws, cfg.T)), got,
+                           b.qsl, cw, cfg.conv_dilation, cfg.eps, conv_state=b.conv_state,
+                           state_out_gpu=host_bits(st_out))
 
 
 def _run_fused_both(cfg, b, L, hidden, *, with_ctx, with_state, max_request_tokens, T=None):
@@ -487,7 +497,7 @@ def _run_fused_both(cfg, b, L, hidden, *, with_ctx, with_state, max_request_toke
                                 gate=gate, workspace=ws, max_request_tokens=max_request_tokens)
     torch.cuda.synchronize()
     return (host_bits(out), gate.cpu().numpy(), host_bits(ple.prefill_conv_input(L, ws, T)), host_bits(st_out),
-            ctx_out.cpu().numpy())
+            ctx_out.cpu().numpy(), host_bits(ple.prefill_kv(L, ws, T)))
 
 
 @pytest.mark.parametrize("case", ["decode-256", "decode-256-fresh", "tiny-empty-requests-k4", "tiny-k1", "tiny-k2",
@@ -539,11 +549,27 @@ def test_decode_tail_equals_plain_path(case):
     log(f"decode tail {case}: T={cfg.T} R={b.R} K={K} d={cfg.conv_dilation} hint={hint}")
     plain = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=0)
     tail = _run_fused_both(cfg, b, L, hidden, with_ctx=not fresh, with_state=not fresh, max_request_tokens=hint)
-    for name, x, y in zip(["out", "gate", "conv input", "state out", "context out"], plain, tail):
+    for name, x, y in zip(["out", "gate", "conv input", "state out", "context out", "kv"], plain, tail):
         np.testing.assert_array_equal(y, x, err_msg=name)
-    if case == "decode-256":  # and against the oracle
-        ref = _oracle_chain(cfg, b, table, scales, kvw, cw, hidden)
-        assert np.abs(bf16_f64(tail[0]) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
+    # and every output against the oracle: the whole chain, then each stage on the tail's own input
+    out_t, gate_t, gated_t, st_t, ctx_t, kv_t = tail
+    state_in = None if fresh else b.conv_state
+    if cfg.T > 0:
+        bb = dataclasses.replace(b, ngram_context=None if fresh else b.ngram_context, conv_state=state_in)
+        ref = _oracle_chain(cfg, bb, table, scales, kvw, cw, hidden)
+        assert np.abs(bf16_f64(out_t) - bf16_f64(ref["y"])).max() <= CONV_ABS_TOL
+        _check_kv(kv_t, ref["kv"], ref["rows"], kvw)
+    check_gate_conv_stages(hidden, kv_t, gate_t, gated_t, out_t, b.qsl, cw, cfg.conv_dilation, cfg.eps,
+                           conv_state=state_in, state_out_gpu=None)
+    # the carried conv state: the last S conv inputs of state ++ the window (the tail's own conv input)
+    _, st_want = oracle.conv(gated_t if cfg.T else np.zeros((0, cfg.N), np.uint16), b.qsl, cw, cfg.conv_dilation,
+                             state=state_in, want_state_out=True)
+    np.testing.assert_array_equal(st_t, st_want)
+    _, ctx_want = oracle.ngram_ids(b.input_ids, b.qsl, b.multipliers[0], b.vocab_sizes, b.offsets,
+                                   context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram,
+                                   eos_token_id=wl.EOS, ngram_context=None if fresh else b.ngram_context,
+                                   want_context_out=True)
+    np.testing.assert_array_equal(ctx_t, ctx_want)
 
 
 def test_wrong_hint_keeps_short_requests_exact():
@@ -756,9 +782,15 @@ def test_prefetch_dedup_equals_prefetch(variant):
     staging = torch.full_like(plain, float("nan"))
     nu = torch.full((1,), -1, dtype=torch.int32, device=DEV)
     ple.ple_prefetch_dedup(L, d_toks, d_qsl, staging, num_unique=nu, ngram_context=ctx)
-    assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
     ids = oracle.ngram_ids(toks, b.qsl, b.multipliers[0], b.vocab_sizes, b.offsets, context_len=cfg.context_len,
                            heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS, ngram_context=b.ngram_context)
+    # against the oracle's gather of the oracle's IDs, then against the plain prefetch
+    if variant == "cfg1-nvfp4":
+        want = oracle.gather_nvfp4(codes, bs, t, ids)
+    else:
+        want = oracle.gather_bf16(table, ids)
+    np.testing.assert_array_equal(host_bits(staging), want.reshape(cfg.T, -1))
+    assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
     assert int(nu.item()) == len(np.unique(ids))
     if variant == "repeats":
         assert int(nu.item()) < ids.size // 2
@@ -767,7 +799,8 @@ def test_prefetch_dedup_equals_prefetch(variant):
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8-global", "nvfp4"])
 def test_prefetch_dedup_rows_of_512(fmt):
     """The deduplicating prefetch on 512-element rows (the scalar-address row stream for fp8 and NVFP4,
-    with the repeated rows skipped by its masked stores) equals the plain prefetch, bit for bit."""
+    with the repeated rows skipped by its masked stores) equals the oracle's gather of the oracle's IDs
+    and the plain prefetch, bit for bit."""
     import dataclasses
     base = wl.CONFIGS[4] if fmt.startswith("fp8") else wl.CONFIGS[3]
     cfg = dataclasses.replace(base, idx=41, T=700, vocab_base=5003)
@@ -775,12 +808,16 @@ def test_prefetch_dedup_rows_of_512(fmt):
     if fmt == "nvfp4":
         codes, bs, t = wl.make_nvfp4_table(cfg.num_rows, cfg.D, cfg.seed)
         tb, keep = _nvfp4_dev(codes, bs, t)
+        gather = lambda ids: oracle.gather_nvfp4(codes, bs, t, ids)  # noqa: E731
     elif fmt == "fp8-global":
         q, _ = wl.make_table(cfg)
         keep = (dev(q), dev(np.asarray([0.0173], np.float32)))
         tb = ple.Table.from_tensor(*keep)
+        gather = lambda ids: oracle.gather_fp8_global(q, np.float32(0.0173), ids)  # noqa: E731
     else:
-        _, _, tb, keep = _table_dev(cfg)
+        q, sc, tb, keep = _table_dev(cfg)
+        gather = (lambda ids: oracle.gather_bf16(q, ids)) if fmt == "bf16" else \
+            (lambda ids: oracle.gather_fp8(q, sc, ids))
     L = ple.Layer(hash_params(b), tb, dev_bf16(wl.make_kv_weight(cfg)), dev_bf16(wl.make_conv_weight(cfg)),
                   conv_dilation=cfg.conv_dilation, eps=cfg.eps)
     d_toks, d_qsl = dev(b.input_ids), dev(b.qsl)
@@ -789,8 +826,9 @@ def test_prefetch_dedup_rows_of_512(fmt):
     staging = torch.full_like(plain, float("nan"))
     nu = torch.full((1,), -1, dtype=torch.int32, device=DEV)
     ple.ple_prefetch_dedup(L, d_toks, d_qsl, staging, num_unique=nu)
-    assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
     ids = oracle_ids(b)
+    np.testing.assert_array_equal(host_bits(staging), gather(ids).reshape(cfg.T, -1))
+    assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
     assert int(nu.item()) == len(np.unique(ids)) < ids.size  # the Zipf batch repeats rows
 
 
@@ -799,7 +837,7 @@ def test_prefetch_dedup_empty_batch_counts_zero():
     b = wl.make_batch(cfg)
     L, table, scales, kvw, cw, keep = _layer(cfg, b)
     nu = torch.full((1,), 5, dtype=torch.int32, device=DEV)
-    staging = torch.empty((1, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
+    staging = torch.empty((0, cfg.H * cfg.D), dtype=torch.bfloat16, device=DEV)
     ple.ple_prefetch_dedup(L, dev(np.zeros(0, np.int32)), dev(np.zeros(1, np.int32)), staging, num_unique=nu)
     assert int(nu.item()) == 0
 

@@ -1,6 +1,10 @@
 """GPU parity at the full benchmark sizes, in the launch configuration the
 benchmark times.  IDs and gathered rows (bf16 copy, fp8 dequant) are compared
-bit-exactly on every token; kv_proj, gate and conv outputs are compared on a
+bit-exactly on every token.  At the 8k prefills (HBM and host-resident
+tables) the whole chain's output is compared with the oracle's on every token
+(the oracle's kv_proj spread over the host cores by rows), and the gate and
+conv stages with the oracle run on the GPU's own kv and conv input; at the
+16k fp8 prefill and for the NVFP4 table the chain is compared on a
 deterministic token sample the oracle computes one by one (the first and last
 tokens of every request plus seeded random tokens, with their conv taps; the
 sizes are in SAMPLE).
@@ -18,7 +22,8 @@ import torch
 import layer_embedding_lookup_amd as ple
 import oracle
 import workloads as wl
-from gpu_util import DEV, bf16_f64, dev, dev_bf16, hash_params, host_bits, log, oracle_ids
+from gpu_util import (DEV, bf16_f64, bf16_ulp_distance, check_gate_conv_stages, dev, dev_bf16, hash_params,
+                      host_bits, log, oracle_ids, oracle_kv_proj_threaded, oracle_threads)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +58,42 @@ def _check_chain(cfg, b, table_h, scales_h, layer, hidden_h, kvw_h, cw_h, got_ou
     assert diff.max() <= OUT_ABS_TOL
 
 
-def _prefill_full(cfg, table_tensor, scales_tensor, table_h, scales_h, layer=1):
+def _check_chain_all(cfg, b, rows_h, layer, hidden_h, kvw_h, cw_h, L, ws, got_out, got_gate):
+    """The whole chain on every token: the oracle's kv_proj (rows spread over
+    the host cores), gate and conv against the GPU's output, max-abs 2e-2;
+    then each stage on the GPU's own input to it (gate at rel 1e-5 on the
+    GPU's kv, conv within one ulp on the GPU's conv input), and the GPU's kv
+    within one ulp wherever the value is not cancelled to near zero."""
+    import time
+    t0 = time.time()
+    log(f"oracle kv_proj on all {cfg.T} tokens ({oracle_threads()} threads)")
+    kv_ref = oracle_kv_proj_threaded(rows_h, kvw_h)
+    log(f"oracle kv_proj done in {time.time() - t0:.1f}s")
+    gated_ref, _ = oracle.gate(hidden_h, kv_ref, cfg.eps)
+    y_ref = oracle.conv(gated_ref, b.qsl, cw_h, cfg.conv_dilation, state=b.conv_state)
+    diff = np.abs(bf16_f64(got_out) - bf16_f64(y_ref))
+    log(f"max |out - oracle| on all {cfg.T} tokens: {diff.max():.4g}")
+    assert diff.max() <= OUT_ABS_TOL
+    kv_gpu = host_bits(ple.prefill_kv(L, ws, cfg.T))
+    d = bf16_ulp_distance(kv_gpu, kv_ref)
+    big = np.abs(bf16_f64(kv_ref)) > 1e-2
+    log(f"kv: {int((d > 0).sum())} of {d.size} elements one or more ulps apart, max {int(d[big].max())} "
+        f"where |kv| > 1e-2")
+    assert d[big].max() <= 1 and (d > 0).mean() < 0.01
+    check_gate_conv_stages(hidden_h, kv_gpu, got_gate, host_bits(ple.prefill_conv_input(L, ws, cfg.T)), got_out,
+                           b.qsl, cw_h, cfg.conv_dilation, cfg.eps, conv_state=b.conv_state)
+    log("gate (rel 1e-5) and conv (one ulp) on the GPU's own stage inputs, every token")
+
+
+def _fused_with_workspace(L, cfg, toks, qsl, hidden, prefetched_rows=None):
+    ws = torch.empty((ple.ple_prefill_workspace_bytes(L, cfg.T),), dtype=torch.uint8, device=DEV)
+    gate = torch.empty((cfg.T,), dtype=torch.float32, device=DEV)
+    out = ple.ple_prefill_fused(L, toks, qsl, hidden, prefetched_rows=prefetched_rows, gate=gate, workspace=ws)
+    torch.cuda.synchronize()
+    return out, gate, ws
+
+
+def _prefill_full(cfg, table_tensor, scales_tensor, table_h, scales_h, layer=1, all_tokens=False):
     b = wl.make_batch(cfg, layers=2)
     log(f"{cfg.name}: T={cfg.T} R={b.R} H={cfg.H} rows={cfg.num_rows}")
     tb = ple.Table.from_tensor(table_tensor, scales_tensor)
@@ -75,15 +115,18 @@ def _prefill_full(cfg, table_tensor, scales_tensor, table_h, scales_h, layer=1):
     cw_h = wl.make_conv_weight(cfg)
     hidden_h = wl.make_hidden(cfg)
     L = ple.Layer(hp, tb, dev_bf16(kvw_h), dev_bf16(cw_h), conv_dilation=cfg.conv_dilation, eps=cfg.eps)
-    out = ple.ple_prefill_fused(L, toks, qsl, dev_bf16(hidden_h))
-    _check_chain(cfg, b, table_h, scales_h, layer, hidden_h, kvw_h, cw_h, host_bits(out))
+    out, gate, ws = _fused_with_workspace(L, cfg, toks, qsl, dev_bf16(hidden_h))
+    if all_tokens:
+        _check_chain_all(cfg, b, want_rows, layer, hidden_h, kvw_h, cw_h, L, ws, host_bits(out), gate.cpu().numpy())
+    else:
+        _check_chain(cfg, b, table_h, scales_h, layer, hidden_h, kvw_h, cw_h, host_bits(out))
 
 
 def test_prefill_8k_bf16_hbm_full():
     cfg = wl.CONFIGS[3]
     log("generating the 8.6 GB table")
     table_h, _ = wl.make_table(cfg)
-    _prefill_full(cfg, dev_bf16(table_h), None, table_h, None)
+    _prefill_full(cfg, dev_bf16(table_h), None, table_h, None, all_tokens=True)
 
 
 def test_prefill_16k_fp8_hbm_full():
@@ -160,18 +203,21 @@ def test_prefill_8k_host_table_full():
             ev = torch.cuda.Event()
             ev.record(side)
             torch.cuda.current_stream().wait_event(ev)
-            out = ple.ple_prefill_fused(L, toks, qsl, dev_bf16(hidden_h), prefetched_rows=staging)
-            torch.cuda.synchronize()
+            out, gate, ws = _fused_with_workspace(L, cfg, toks, qsl, dev_bf16(hidden_h), prefetched_rows=staging)
         finally:
             ple.ple_stream_destroy(side)
-        _check_chain(cfg, b, table_h, None, layer, hidden_h, kvw_h, cw_h, host_bits(out))
-        # distinct rows only across the host link: the same staging, bit for bit
+        want_ids = oracle_ids(b, layer)
+        want_rows = table_h[want_ids.reshape(-1)].reshape(cfg.T, -1)
+        np.testing.assert_array_equal(host_bits(staging), want_rows)
+        _check_chain_all(cfg, b, want_rows, layer, hidden_h, kvw_h, cw_h, L, ws, host_bits(out), gate.cpu().numpy())
+        # distinct rows only across the host link: the oracle's rows, bit for bit
         staging2 = torch.empty_like(staging)
         nu = torch.zeros((1,), dtype=torch.int32, device=DEV)
         ple.ple_prefetch_dedup(L, toks, qsl, staging2, num_unique=nu)
         torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(staging2), want_rows)
         assert torch.equal(staging2.view(torch.int16), staging.view(torch.int16))
-        n_unique = len(np.unique(oracle_ids(b, layer)))
+        n_unique = len(np.unique(want_ids))
         assert int(nu.item()) == n_unique
         log(f"dedup prefetch bit-exact; {n_unique} of {cfg.T * cfg.H} rows distinct")
     finally:
