@@ -76,6 +76,8 @@ extern "C" {
 #define PLE_MAX_HEADS 32
 #define PLE_MAX_CONTEXT 7
 #define PLE_MAX_TOKENS (1 << 24) /* tokens per call */
+/* bytes of the library-owned scratch array behind ple_prefill_fused_noalloc (64 MiB per GPU) */
+#define PLE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * Hash constants of one layer ([P3] 关键源码片段: layer multipliers, per-head
@@ -265,6 +267,27 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
                       const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* workspace,
                       size_t workspace_bytes, void* stream);
 size_t ple_prefill_workspace_bytes(const ple_layer_desc* layer, int64_t max_tokens);
+
+/*
+ * ple_prefill_fused for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same launches and the same results, bit for bit, as
+ * ple_prefill_fused with the same arguments, but the intermediates (rows, kv,
+ * conv input) go to a scratch array the library owns: PLE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) of device memory on each GPU the library runs on, held from the
+ * time the library's code is loaded on that GPU until the process ends.  This
+ * call allocates and frees nothing.
+ * Limit: ple_prefill_workspace_bytes(layer, T) <= PLE_NOALLOC_SCRATCH_BYTES
+ * (for H*D = N = 4096, up to 2047 tokens; for H*D = N = 2048, up to 4095),
+ * else PLE_ERR_WORKSPACE before any device work.
+ * Every call on one GPU shares that GPU's array and leaves it holding its own
+ * intermediates: calls whose work overlaps on one GPU (other streams, other
+ * host threads) race and give unspecified results; order them on one stream.
+ * The conv input is not handed back (use ple_prefill_fused with a workspace
+ * to read it, e.g. for ple_spec_commit).
+ */
+int ple_prefill_fused_noalloc(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
+                              const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* stream);
 
 /*
  * Pinned host memory the GPU reads directly ([P1] 功能与动机 and 关键源码片段,

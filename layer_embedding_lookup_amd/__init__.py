@@ -30,6 +30,7 @@ __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_l
            "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes", "ple_dp_gather_slot", "ple_head_shard",
            "ple_select_rows",
            "ple_kv_proj", "ple_gate", "ple_conv", "ple_spec_commit", "ple_prefill_fused", "ple_prefill_workspace_bytes",
+           "ple_prefill_fused_noalloc",
            "prefill_conv_input", "prefill_kv",
            "ple_host_alloc", "ple_host_free", "HostBuffer", "ple_stream_create_cu_masked", "ple_stream_destroy",
            "ple_error_message", "ple_version", "library"]
@@ -453,6 +454,28 @@ def ple_prefill_fused(layer: Layer, input_ids, query_start_loc, hidden, *, prefe
     capi.check(capi.load().ple_prefill_fused(ctypes.byref(L), ctypes.byref(b), _ptr(hidden), _ptr(prefetched_rows),
                                              _ptr(out), _ptr(gate), _ptr(workspace), _nbytes(workspace),
                                              _stream(stream)), "ple_prefill_fused")
+    return out
+
+
+def ple_prefill_fused_noalloc(layer: Layer, input_ids, query_start_loc, hidden, *, prefetched_rows=None,
+                              ngram_context=None, ngram_context_out=None, conv_state=None, conv_state_out=None,
+                              out, gate=None, max_request_tokens=0, stream=None):
+    """ple_prefill_fused with its intermediates in the library's own scratch array (no workspace,
+    no allocation by the library; `out` is the caller's)."""
+    _req("hidden", hidden, (None, layer.hidden), _BF16)
+    T, N = hidden.shape
+    _req("input_ids", input_ids, (T,), _I32)
+    _req("prefetched_rows", prefetched_rows, (T, layer.hash.num_heads * layer.table.dim), _BF16, optional=True)
+    _req("out", out, (T, N), _BF16)
+    _req("gate", gate, (T,), _F32, optional=True)
+    L = layer.desc()
+    S = (layer.conv_kernel - 1) * layer.conv_dilation
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, conv_state, conv_state_out,
+               max_request_tokens=max_request_tokens, context_len=layer.hash.context_len, state_shape=(S, N))
+    _same_device(input_ids, hidden, prefetched_rows, out, gate, layer.kv_weight, layer.conv_weight)
+    capi.check(capi.load().ple_prefill_fused_noalloc(ctypes.byref(L), ctypes.byref(b), _ptr(hidden),
+                                                     _ptr(prefetched_rows), _ptr(out), _ptr(gate), _stream(stream)),
+               "ple_prefill_fused_noalloc")
     return out
 
 

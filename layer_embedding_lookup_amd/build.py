@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libple.so")
 SOURCES = ["ple_api.cpp", "ple_lookup.hip", "ple_kv_proj.hip", "ple_gate_conv.hip", "ple_dedup.hip", "ple_dp.hip",
-           "ple_spec.hip"]
+           "ple_spec.hip", "ple_static.hip"]
 ARCH = "gfx950"
 
 

@@ -26,6 +26,7 @@ PLE_DTYPE_FP8_E4M3_GLOBAL = 2
 PLE_DTYPE_NVFP4 = 3
 PLE_MAX_HEADS = 32
 PLE_MAX_CONTEXT = 7
+PLE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 P = ctypes.c_void_p
 I32 = ctypes.c_int32
@@ -74,6 +75,8 @@ _PROTOS = {
     "ple_prefill_fused": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P, P, P,
                                          P, P, ctypes.c_size_t, P]),
     "ple_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ple_layer_desc), I64]),
+    "ple_prefill_fused_noalloc": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P,
+                                                 P, P, P, P]),
     "ple_host_alloc": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(P), ctypes.POINTER(P)]),
     "ple_host_free": (ctypes.c_int, [P]),
     "ple_stream_create_cu_masked": (ctypes.c_int, [I32, ctypes.POINTER(P)]),

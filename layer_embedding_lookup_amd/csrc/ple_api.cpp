@@ -747,6 +747,29 @@ int ple_prefill_fused(const ple_layer_desc* layer, const ple_batch_desc* batch, 
     return rc ? rc : ok();
 }
 
+int ple_prefill_fused_noalloc(const ple_layer_desc* layer, const ple_batch_desc* batch, const uint16_t* hidden,
+                              const uint16_t* prefetched_rows, uint16_t* out, float* gate, void* stream) {
+    HashParams hp;
+    int cpr_log2 = -1;
+    int rc = prefill_checks(layer, batch, hidden, prefetched_rows, out, gate, &hp, &cpr_log2);
+    if (rc) return rc;
+    const size_t need = ple_prefill_workspace_bytes(layer, batch->num_tokens);
+    if (need > (size_t)PLE_NOALLOC_SCRATCH_BYTES)
+        return fail(PLE_ERR_WORKSPACE,
+                    "ple_prefill_fused_noalloc: %lld tokens need %zu bytes of intermediates, more than the "
+                    "library's %zu-byte scratch array (use ple_prefill_fused with a workspace)",
+                    (long long)batch->num_tokens, need, (size_t)PLE_NOALLOC_SCRATCH_BYTES);
+    if (!prefill_has_work(layer, batch, prefetched_rows)) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    void* scratch = nullptr;
+    hipError_t e = noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    rc = prefill_run(layer, batch, hp, cpr_log2, hidden, prefetched_rows, out, gate, (char*)scratch,
+                     (hipStream_t)stream);
+    return rc ? rc : ok();
+}
+
 int ple_host_alloc(size_t bytes, void** host, void** device) {
     if (bytes == 0 || host == nullptr || device == nullptr)
         return fail(PLE_ERR_INVALID_ARGUMENT, "ple_host_alloc needs bytes > 0 and non-NULL outputs");

@@ -45,6 +45,10 @@ hipError_t launch_dedup_copy(const int32_t* rep_of, int64_t n, int dim, uint16_t
 hipError_t launch_select_rows(const uint16_t* gathered, int E, int64_t slot, int rank, int64_t n, int width,
                               uint16_t* out, hipStream_t s);
 
+// Device address of the current device's copy of the library's scratch array
+// (PLE_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K, int O, uint16_t* kv,
                           hipStream_t s);
 

@@ -21,7 +21,7 @@ FAKE = 1 << 40  # a 256-aligned address that is never dereferenced: every call b
 
 def test_exports_every_header_function():
     names = capi.header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(capi._PROTOS)
@@ -215,3 +215,22 @@ def test_spec_commit_rejects_and_noops():
     b_alias = _batch(state=FAKE + 256, state_out=FAKE + 256)
     assert lib.ple_spec_commit(None, ctypes.byref(b_alias), acc, FAKE, 16, 4, 1, None) == E_ARG
     assert "alias" in _msg()
+
+
+def test_prefill_noalloc_rejects_beyond_its_scratch():
+    """The allocation-free fused prefill takes at most PLE_NOALLOC_SCRATCH_BYTES of intermediates and
+    says so before any device work; its argument checks are those of ple_prefill_fused."""
+    L, keep = _layer()
+    # 128-wide rows, kv and conv input: (128 + 256 + 128) * 2 bytes per token
+    per_token = (128 + 256 + 128) * 2
+    T = capi.PLE_NOALLOC_SCRATCH_BYTES // per_token + 1
+    b = capi.ple_batch_desc(FAKE, FAKE, T, 4, 0, None, None, None, None)
+    assert lib.ple_prefill_fused_noalloc(ctypes.byref(L), ctypes.byref(b), FAKE, None, FAKE + 256, None,
+                                         None) == E_WS
+    assert "scratch" in _msg()
+    L3, keep3 = _layer(eps=-1.0)
+    b = _batch(T=24, R=4)
+    assert lib.ple_prefill_fused_noalloc(ctypes.byref(L3), ctypes.byref(b), FAKE, None, FAKE, None, None) == E_ARG
+    assert lib.ple_prefill_fused_noalloc(None, ctypes.byref(b), FAKE, None, FAKE, None, None) == E_ARG
+    L2, keep2 = _layer(N=100)
+    assert lib.ple_prefill_fused_noalloc(ctypes.byref(L2), ctypes.byref(b), FAKE, None, FAKE, None, None) == E_UNSUP
