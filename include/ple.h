@@ -251,10 +251,15 @@ int ple_conv(const uint16_t* x, const ple_batch_desc* batch, const uint16_t* w, 
  * or NULL; workspace: device memory of at least
  * ple_prefill_workspace_bytes(layer, T) bytes, 256-byte aligned (holds rows,
  * kv and the gated value between kernels; not read before being written).
- * On return the conv input (the gated value, bf16 [T][N]) stays in the
- * workspace at byte offset round256(T*H*D*2) + round256(T*2N*2), where
- * round256 rounds up to a multiple of 256 and T = batch->num_tokens: a
- * speculative verify step that keeps one workspace per layer passes that
+ * The conv input of token t (the gated value g * v rounded to bf16, N
+ * values) is formed inside the conv; on return the conv inputs of each
+ * request's last S tokens (S = (Kc-1)*d), and of every token of a request
+ * of at most max(S, 16) tokens (every token when the decode tail below runs),
+ * stay in the workspace as rows t of a bf16 [T][N] region at byte offset
+ * round256(T*H*D*2) + round256(T*2N*2), where round256 rounds up to a
+ * multiple of 256 and T = batch->num_tokens; the other rows of the region
+ * are unspecified.  A speculative verify step whose windows hold at most
+ * max(S, 16) tokens and that keeps one workspace per layer passes that
  * region as x to ple_spec_commit.
  * With batch->max_request_tokens in 1..4 (a decode step or speculative
  * verify windows: no request has more tokens), Kc <= 4 and N <= 8192, gate,

@@ -410,7 +410,9 @@ def ple_prefill_workspace_bytes(layer: Layer, max_tokens: int) -> int:
 
 
 def prefill_conv_input(layer: Layer, workspace, num_tokens: int):
-    """View of the conv input (gated value, bf16 [T][N]) a ple_prefill_fused call leaves in its workspace."""
+    """View of the conv input region (gated values, bf16 [T][N]) a ple_prefill_fused call leaves in its
+    workspace: rows of each request's last S tokens and of requests of at most max(S, 16) tokens are
+    set (every row after the decode tail)."""
     def r256(n):
         return (n + 255) // 256 * 256
     T, N = int(num_tokens), layer.hidden

@@ -15,6 +15,10 @@
 
 using namespace ple;
 
+#ifndef PLE_FUSED_GATED_CONV
+#define PLE_FUSED_GATED_CONV 1  // the fused path forms the gated value inside the conv
+#endif
+
 namespace {
 
 thread_local char g_msg[512];
@@ -600,7 +604,7 @@ size_t ple_prefill_workspace_bytes(const ple_layer_desc* layer, int64_t max_toke
     const size_t T = (size_t)max_tokens;
     const size_t HD = (size_t)layer->hash.num_heads * (size_t)layer->table.dim;
     const size_t N = (size_t)layer->hidden;
-    return round256(T * HD * 2) + round256(T * 2 * N * 2) + round256(T * N * 2);
+    return round256(T * HD * 2) + round256(T * 2 * N * 2) + round256(T * N * 2) + round256(T * 4);
 }
 
 }  // extern "C"
@@ -696,11 +700,32 @@ int prefill_run(const ple_layer_desc* layer, const ple_batch_desc* batch, const 
         if (e != hipSuccess) return hip_fail(e, "decode tail launch");
         return PLE_OK;
     }
-    if (T > 0) {
+    if (T > 0 && PLE_FUSED_GATED_CONV && conv_rows_supported(layer->conv_kernel, N)) {
+        // the gate alone, then the conv on the value half of kv, gated as it
+        // is read: the gated value makes no round trip through memory; only
+        // the conv inputs the carried state or a verify commit may take are
+        // written to the workspace
+        float* g = (float*)((char*)gated + round256((size_t)T * N * 2));
+        e = launch_gate_only(hidden, kv, T, N, layer->eps, g, gate, s);
+        if (e != hipSuccess) return hip_fail(e, "gate launch");
+        ConvRowsArgs ca = {};
+        ca.x = kv + N;
+        ca.x_stride = 2 * (int64_t)N;
+        ca.g = g;
+        ca.qsl = batch->query_start_loc;
+        ca.T = T;
+        ca.R = batch->num_reqs;
+        ca.state = batch->conv_state;
+        ca.w = layer->conv_weight;
+        ca.N = N;
+        ca.d = layer->conv_dilation;
+        ca.y = out;
+        ca.gated_out = gated;
+        e = launch_conv_gated(ca, layer->conv_kernel, s);
+        if (e != hipSuccess) return hip_fail(e, "conv launch");
+    } else if (T > 0) {
         e = launch_gate(hidden, kv, T, N, layer->eps, gated, gate, s);
         if (e != hipSuccess) return hip_fail(e, "gate launch");
-    }
-    if (T > 0) {
         e = launch_conv(gated, batch->query_start_loc, T, batch->num_reqs, batch->conv_state, layer->conv_weight, N,
                         layer->conv_kernel, layer->conv_dilation, out, s);
         if (e != hipSuccess) return hip_fail(e, "conv launch");

@@ -74,10 +74,13 @@ __device__ __forceinline__ u32x4 gate_chunk(float g, u32x4 x) {
                  pack_bf16x2(g * bf16_lo(x.z), g * bf16_hi(x.z)), pack_bf16x2(g * bf16_lo(x.w), g * bf16_hi(x.w))};
 }
 
-template <int UNROLL>
+// SCALE: also write out = bf16(g * v); otherwise only the gate (into gate and,
+// when given, gate2: the fused path's own copy and the caller's).
+template <int UNROLL, bool SCALE>
 __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ hidden,
                                                    const uint16_t* __restrict__ kv, int64_t T, int N, float eps,
-                                                   uint16_t* __restrict__ out, float* __restrict__ gate) {
+                                                   uint16_t* __restrict__ out, float* __restrict__ gate,
+                                                   float* __restrict__ gate2) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave; no block-level barrier below
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
 
     // a row of at most 64 x UNROLL chunks is one pass: its value half is
     // loaded with h and k, so the wave makes one round trip, not two
-    const bool one_pass = nch <= 64 * UNROLL;
+    const bool one_pass = SCALE && nch <= 64 * UNROLL;
     u32x4 vpre[UNROLL];
     float hh = 0.f, kk = 0.f, hk = 0.f;
     for (int base = lane; base < nch; base += 64 * UNROLL) {
@@ -115,6 +118,8 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
     }
     const float g = token_gate(hh, kk, hk, N, eps);
     if (lane == 0 && gate != nullptr) gate[t] = g;
+    if (lane == 0 && gate2 != nullptr) gate2[t] = g;
+    if (!SCALE) return;
 
     for (int base = lane; base < nch; base += 64 * UNROLL) {
         u32x4 vv[UNROLL];
@@ -339,20 +344,25 @@ __global__ __launch_bounds__(256) void conv_lds_kernel(const uint16_t* __restric
 // speculatively together with the request lookup (one round trip); taps that
 // fall before the request start are then replaced by the carried state (or
 // zero).
-template <int KC, int CPL>
-__global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ qsl, int64_t T, int R,
-                                                        const uint16_t* __restrict__ state,
-                                                        const uint16_t* __restrict__ w, int N, int d,
-                                                        uint16_t* __restrict__ y) {
+// GATED: the conv input of token p is bf16(g[p] * v[p]) with v[p] the value
+// half of kv's row p (row stride x_stride), formed here with the gate's own
+// arithmetic (gate_chunk), so the gated value never goes through memory;
+// carried-state rows are conv inputs already.  With gated_out, the conv
+// inputs of each request's last S tokens (the rows the carried state takes)
+// and of every token of a request of at most kConvInputWindow tokens (a
+// speculative verify window) are written there.
+template <int KC, int CPL, bool GATED>
+__global__ __launch_bounds__(256) void conv_rows_kernel(ConvRowsArgs a) {
     // weights [N][KC] = nch x KC 16-byte chunks, kept in LDS tap-chunk-major
     // (s_wv[q * nch + c]) so that consecutive lanes read consecutive chunks
     extern __shared__ u32x4 s_wv[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid >> 6;
+    const int N = a.N;
     const int nch = N >> 3;
-    const int64_t S = (int64_t)(KC - 1) * d;
+    const int64_t T = a.T;
+    const int64_t S = (int64_t)(KC - 1) * a.d;
     const int xcd = blockIdx.x & 7;
     const int64_t blocks_per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
     const int64_t per_xcd = (T + 7) / 8;
@@ -364,29 +374,38 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     // the first token's query_start_loc probe goes out with the weight
     // staging, so that its round trip overlaps the staging's
     QslProbe qp;
-    qsl_probe_load(qsl, R, lane, qp);
+    qsl_probe_load(a.qsl, a.R, lane, qp);
     for (int i = tid; i < nch * KC; i += 256) {
         const int c = i / KC, q = i - (i / KC) * KC;
-        s_wv[q * nch + c] = ((const u32x4*)w)[i];
+        s_wv[q * nch + c] = ((const u32x4*)a.w)[i];
     }
     __syncthreads();
 
     for (int64_t t = t_first; t < t_end; t += stride) {
         int r = 0;
-        int64_t a = 0;
+        int64_t ra = 0;
         if (t == t_first)
-            wave_find_request_probed(qsl, qp, R, t, t, 1, 0, lane, r, a);
+            wave_find_request_probed(a.qsl, qp, a.R, t, t, 1, 0, lane, r, ra);
         else
-            wave_find_request(qsl, R, t, t, 1, 0, lane, r, a);
+            wave_find_request(a.qsl, a.R, t, t, 1, 0, lane, r, ra);
         // tap i of this token: the batch row t - i*d within the request, else
         // the carried state row (oldest first), else zero; resolved before any
         // load, so each pass is one round trip
         const uint16_t* src[KC];
+        float gs[KC];
 #pragma unroll
         for (int i = 0; i < KC; ++i) {
-            const int64_t p = t - (int64_t)i * d;
-            src[i] = p >= a ? x + p * N
-                            : (state != nullptr ? state + ((int64_t)r * S + (S - (a - p))) * N : nullptr);
+            const int64_t p = t - (int64_t)i * a.d;
+            src[i] = p >= ra ? a.x + p * a.x_stride
+                             : (a.state != nullptr ? a.state + ((int64_t)r * S + (S - (ra - p))) * N : nullptr);
+            gs[i] = 1.f;
+            if (GATED && p >= ra) gs[i] = a.g[p];
+        }
+        bool keep = false;  // this token's conv input goes to gated_out
+        if (GATED && a.gated_out != nullptr) {
+            int64_t rb = a.qsl[r + 1];
+            rb = rb < t + 1 ? t + 1 : rb;
+            keep = t >= rb - S || rb - ra <= kConvInputWindow;
         }
         for (int cb = 0; cb < nch; cb += kWave * CPL) {
             u32x4 xv[CPL][KC];
@@ -404,13 +423,19 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
             for (int j = 0; j < CPL; ++j) {
                 const int c = cb + j * kWave + lane;
                 if (c < nch) {
+                    if (GATED) {
+#pragma unroll
+                        for (int i = 0; i < KC; ++i)
+                            if (t - (int64_t)i * a.d >= ra) xv[j][i] = gate_chunk(gs[i], xv[j][i]);
+                        if (keep) *(u32x4*)(a.gated_out + t * N + (int64_t)c * 8) = xv[j][0];
+                    }
                     u32x4 wq[KC];
 #pragma unroll
                     for (int q = 0; q < KC; ++q) wq[q] = s_wv[q * nch + c];
 #if PLE_CONV_NT_STORE
-                    __builtin_nontemporal_store(conv_chunk<KC>(wq, xv[j]), (u32x4*)(y + t * N + (int64_t)c * 8));
+                    __builtin_nontemporal_store(conv_chunk<KC>(wq, xv[j]), (u32x4*)(a.y + t * N + (int64_t)c * 8));
 #else
-                    *(u32x4*)(y + t * N + (int64_t)c * 8) = conv_chunk<KC>(wq, xv[j]);
+                    *(u32x4*)(a.y + t * N + (int64_t)c * 8) = conv_chunk<KC>(wq, xv[j]);
 #endif
                 }
             }
@@ -418,11 +443,10 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(const uint16_t* __restri
     }
 }
 
-template <int KC, int CPL>
-static hipError_t launch_conv_rows_t(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
-                                     const uint16_t* w, int N, int d, uint16_t* y, hipStream_t s) {
-    const size_t lds = (size_t)N * KC * 2;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)conv_rows_kernel<KC, CPL>,
+template <int KC, int CPL, bool GATED>
+static hipError_t launch_conv_rows_t(const ConvRowsArgs& a, hipStream_t s) {
+    const size_t lds = (size_t)a.N * KC * 2;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)conv_rows_kernel<KC, CPL, GATED>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (attr != hipSuccess) return attr;
     // resident blocks per device for this kernel and weight size (queried once)
@@ -437,7 +461,7 @@ static hipError_t launch_conv_rows_t(const uint16_t* x, const int32_t* qsl, int6
         if (it == resident.end()) {
             int cus = 256, per_cu = 1;
             (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC, CPL>, 256, lds) !=
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_rows_kernel<KC, CPL, GATED>, 256, lds) !=
                     hipSuccess ||
                 per_cu < 1)
                 per_cu = 1;
@@ -445,22 +469,33 @@ static hipError_t launch_conv_rows_t(const uint16_t* x, const int32_t* qsl, int6
         }
         blocks = it->second;                                 // every block resident at once
     }
-    const int64_t need = (T + 3) / 4;                        // one wave per token at most
+    const int64_t need = (a.T + 3) / 4;                      // one wave per token at most
     if (blocks > need) blocks = need;
     blocks = ((blocks + 7) / 8) * 8;                         // whole XCD rounds
-    hipLaunchKernelGGL((conv_rows_kernel<KC, CPL>), dim3((unsigned)blocks), dim3(256), lds, s, x, qsl, T, R, state, w,
-                       N, d, y);
+    hipLaunchKernelGGL((conv_rows_kernel<KC, CPL, GATED>), dim3((unsigned)blocks), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
 // Rows of at most 256 16-byte chunks (N <= 2048) go in one pass of 4 chunks
 // per lane, so a token costs one round trip; wider rows take passes of 2
 // (measured best for the 4096-wide prefill).
-template <int KC>
-static hipError_t launch_conv_rows(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
-                                   const uint16_t* w, int N, int d, uint16_t* y, hipStream_t s) {
-    if ((N >> 3) <= 4 * kWave) return launch_conv_rows_t<KC, 4>(x, qsl, T, R, state, w, N, d, y, s);
-    return launch_conv_rows_t<KC, PLE_CONV_CPL>(x, qsl, T, R, state, w, N, d, y, s);
+template <int KC, bool GATED>
+static hipError_t launch_conv_rows(const ConvRowsArgs& a, hipStream_t s) {
+    if ((a.N >> 3) <= 4 * kWave) return launch_conv_rows_t<KC, 4, GATED>(a, s);
+    return launch_conv_rows_t<KC, PLE_CONV_CPL, GATED>(a, s);
+}
+
+bool conv_rows_supported(int K, int N) { return K >= 1 && K <= 4 && (size_t)N * K * 2 <= 64 * 1024; }
+
+hipError_t launch_conv_gated(const ConvRowsArgs& a, int K, hipStream_t s) {
+    if (a.T <= 0) return hipSuccess;
+    switch (K) {
+        case 1: return launch_conv_rows<1, true>(a, s);
+        case 2: return launch_conv_rows<2, true>(a, s);
+        case 3: return launch_conv_rows<3, true>(a, s);
+        case 4: return launch_conv_rows<4, true>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // state_out[r][m] = the (S-m)-th most recent conv input of state[r] ++ x[a:b].
@@ -675,19 +710,38 @@ hipError_t launch_decode_tail(const DecodeTailArgs& a, int K, hipStream_t s) {
 hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, uint16_t* out,
                        float* gate, hipStream_t s) {
     const int64_t blocks = (T + 3) / 4;
-    hipLaunchKernelGGL(gate_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, hidden, kv, T, N, eps, out, gate);
+    hipLaunchKernelGGL((gate_kernel<8, true>), dim3((unsigned)blocks), dim3(256), 0, s, hidden, kv, T, N, eps, out,
+                       gate, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_only(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, float* g,
+                            float* gate, hipStream_t s) {
+    const int64_t blocks = (T + 3) / 4;
+    hipLaunchKernelGGL((gate_kernel<8, false>), dim3((unsigned)blocks), dim3(256), 0, s, hidden, kv, T, N, eps,
+                       nullptr, g, gate);
     return hipGetLastError();
 }
 
 hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
                        const uint16_t* w, int N, int K, int d, uint16_t* y, hipStream_t s) {
-    if ((size_t)N * K * 2 <= 64 * 1024) {
+    if (conv_rows_supported(K, N)) {
+        ConvRowsArgs a = {};
+        a.x = x;
+        a.x_stride = N;
+        a.qsl = qsl;
+        a.T = T;
+        a.R = R;
+        a.state = state;
+        a.w = w;
+        a.N = N;
+        a.d = d;
+        a.y = y;
         switch (K) {
-            case 1: return launch_conv_rows<1>(x, qsl, T, R, state, w, N, d, y, s);
-            case 2: return launch_conv_rows<2>(x, qsl, T, R, state, w, N, d, y, s);
-            case 3: return launch_conv_rows<3>(x, qsl, T, R, state, w, N, d, y, s);
-            case 4: return launch_conv_rows<4>(x, qsl, T, R, state, w, N, d, y, s);
-            default: break;
+            case 1: return launch_conv_rows<1, false>(a, s);
+            case 2: return launch_conv_rows<2, false>(a, s);
+            case 3: return launch_conv_rows<3, false>(a, s);
+            default: return launch_conv_rows<4, false>(a, s);
         }
     }
     constexpr int TB = PLE_CONV_TOKENS_PER_BLOCK;

@@ -81,6 +81,31 @@ hipError_t launch_decode_tail(const DecodeTailArgs& a, int K, hipStream_t s);
 
 hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, uint16_t* out,
                        float* gate, hipStream_t s);
+// The gate alone: g[t] (and gate[t] when non-NULL), same arithmetic as launch_gate.
+hipError_t launch_gate_only(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, float* g,
+                            float* gate, hipStream_t s);
+
+// Row-wise convolution (kernel sizes 1-4, N * K * 2 <= 64 KiB of weights):
+// conv input of token p = x + p * x_stride (elements), or, gated,
+// bf16(g[p] * x[p]) with the gate's arithmetic.
+constexpr int kConvInputWindow = 16;  // requests this short keep every conv input (verify windows)
+struct ConvRowsArgs {
+    const uint16_t* x;
+    int64_t x_stride;
+    const float* g;          // [T], gated only
+    const int32_t* qsl;
+    int64_t T;
+    int32_t R;
+    const uint16_t* state;   // [R][S][N] or NULL
+    const uint16_t* w;       // [N][K]
+    int32_t N;
+    int32_t d;
+    uint16_t* y;             // [T][N]
+    uint16_t* gated_out;     // gated only, [T][N] or NULL: conv inputs of each request's last S tokens and
+                             // of every token of a request of at most kConvInputWindow tokens
+};
+bool conv_rows_supported(int K, int N);
+hipError_t launch_conv_gated(const ConvRowsArgs& a, int K, hipStream_t s);
 hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, const uint16_t* state,
                        const uint16_t* w, int N, int K, int d, uint16_t* y, hipStream_t s);
 hipError_t launch_conv_state_out(const uint16_t* x, const int32_t* qsl, int64_t T, int R,

@@ -38,6 +38,9 @@
 #ifndef PLE_LOOKUP_NT_STORE_BF16
 #define PLE_LOOKUP_NT_STORE_BF16 0
 #endif
+#ifndef PLE_LOOKUP_NT_LOAD_BF16
+#define PLE_LOOKUP_NT_LOAD_BF16 1
+#endif
 #ifndef PLE_LOOKUP_NT_STORE_QUANT
 #define PLE_LOOKUP_NT_STORE_QUANT 1
 #endif
@@ -278,7 +281,7 @@ __device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const Stre
                 const int ch = idx - row * a.cpr;
                 const char* src = a.table + (int64_t)rid * row_bytes + (int64_t)ch * IB;
                 if (DTYPE == kFmtBF16) {
-                    v[u] = __builtin_nontemporal_load((const u32x4*)src);
+                    v[u] = PLE_LOOKUP_NT_LOAD_BF16 ? __builtin_nontemporal_load((const u32x4*)src) : *(const u32x4*)src;
                 } else if (DTYPE == kFmtFP8) {
                     const u32x2 q = __builtin_nontemporal_load((const u32x2*)src);
                     v[u] = u32x4{q.x, q.y, 0u, 0u};

@@ -15,7 +15,7 @@ import layer_embedding_lookup_amd as ple
 import oracle
 import workloads as wl
 from gpu_util import (DEV, bf16_f64, bf16_ulp_distance, check_gate_conv_stages, dev, dev_bf16, hash_params,
-                      host_bits, log, oracle_ids)
+                      host_bits, last_rows_of_requests, log, oracle_ids)
 
 pytestmark = pytest.mark.gpu
 
@@ -477,9 +477,14 @@ def test_prefill_fused_parity_small(variant):
     np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
     kv_gpu = host_bits(ple.prefill_kv(L, ws, cfg.T))
     _check_kv(kv_gpu, ref["kv"], ref["rows"], kvw)
-    check_gate_conv_stages(hidden, kv_gpu, gate.cpu().numpy(), host_bits(ple.prefill_conv_input(L, ws, cfg.T)), got,
-                           b.qsl, cw, cfg.conv_dilation, cfg.eps, conv_state=b.conv_state,
-                           state_out_gpu=host_bits(st_out))
+    written = last_rows_of_requests(b.qsl, cfg.S, cfg.T)
+    gated_ws = host_bits(ple.prefill_conv_input(L, ws, cfg.T))
+    check_gate_conv_stages(hidden, kv_gpu, gate.cpu().numpy(), gated_ws, got, b.qsl, cw, cfg.conv_dilation, cfg.eps,
+                           conv_state=b.conv_state, state_out_gpu=host_bits(st_out), gated_rows=written)
+    # the carried state is a copy of the conv inputs the GPU left in the workspace
+    _, st_copy = oracle.conv(np.where(written[:, None], gated_ws, 0).astype(np.uint16), b.qsl, cw, cfg.conv_dilation,
+                             state=b.conv_state, want_state_out=True)
+    np.testing.assert_array_equal(host_bits(st_out), st_copy)
 
 
 def _run_fused_both(cfg, b, L, hidden, *, with_ctx, with_state, max_request_tokens, T=None):

@@ -23,7 +23,7 @@ import layer_embedding_lookup_amd as ple
 import oracle
 import workloads as wl
 from gpu_util import (DEV, bf16_f64, bf16_ulp_distance, check_gate_conv_stages, dev, dev_bf16, hash_params,
-                      host_bits, log, oracle_ids, oracle_kv_proj_threaded, oracle_threads)
+                      host_bits, last_rows_of_requests, log, oracle_ids, oracle_kv_proj_threaded, oracle_threads)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,8 +81,9 @@ def _check_chain_all(cfg, b, rows_h, layer, hidden_h, kvw_h, cw_h, L, ws, got_ou
         f"where |kv| > 1e-2")
     assert d[big].max() <= 1 and (d > 0).mean() < 0.01
     check_gate_conv_stages(hidden_h, kv_gpu, got_gate, host_bits(ple.prefill_conv_input(L, ws, cfg.T)), got_out,
-                           b.qsl, cw_h, cfg.conv_dilation, cfg.eps, conv_state=b.conv_state)
-    log("gate (rel 1e-5) and conv (one ulp) on the GPU's own stage inputs, every token")
+                           b.qsl, cw_h, cfg.conv_dilation, cfg.eps, conv_state=b.conv_state,
+                           gated_rows=last_rows_of_requests(b.qsl, cfg.S, cfg.T))
+    log("gate (rel 1e-5) on the GPU's kv and conv on it, every token")
 
 
 def _fused_with_workspace(L, cfg, toks, qsl, hidden, prefetched_rows=None):
