@@ -130,8 +130,9 @@ def _layer(N=128, Kc=4, d=2, kvw=FAKE, convw=FAKE, eps=1e-6):
 def test_prefill_workspace():
     L, keep = _layer()
     need = lib.ple_prefill_workspace_bytes(ctypes.byref(L), 24)
-    # rows 24 x 128 bf16, kv 24 x 256 bf16, gated 24 x 128 bf16, each rounded up to 256 bytes
-    assert need == 6144 + 12288 + 6144
+    # rows 24 x 128 bf16, kv 24 x 256 bf16, conv input 24 x 128 bf16, gate 24 fp32, each rounded up
+    # to 256 bytes
+    assert need == 6144 + 12288 + 6144 + 256
     b = _batch(T=24, R=4)
     rc = lib.ple_prefill_fused(ctypes.byref(L), ctypes.byref(b), FAKE, None, FAKE, None, FAKE, need - 1, None)
     assert rc == E_WS
