@@ -199,13 +199,34 @@ def main() -> int:
         torch_gather_ms = timed(lambda i: torch.index_select(table, 0, ids_l[i % L],
                                                             out=outs[i % len(outs)].view(T * H, D)), 4 * L)
         del ids_l
-    # streaming-copy ceiling: a device-to-device copy of 1 GiB (four times the
-    # last-level cache, so the copy streams from and to HBM)
-    copy_src = torch.empty((1 << 29,), dtype=torch.bfloat16, device=dev)
-    copy_dst = torch.empty_like(copy_src)
-    copy_ms = timed(lambda i: copy_dst.copy_(copy_src), 4)
-    copy_gbps = 2 * copy_src.numel() * 2 / (copy_ms * 1e-3) / 1e9
-    del copy_src, copy_dst
+    # Streaming-copy ceilings (libple_bench, hand-written 16-byte copies, one
+    # pass per wave): the lookup's 64 MiB of output copied contiguously from
+    # rotating 64 MiB windows of the table, and the same random rows the
+    # lookup reads (this layer's IDs) gathered into the same rotating outputs
+    blib = bench_library()
+    out_bytes = T * H * D * 2
+    row_bytes_in = {"bf16": D * 2, "fp8": D, "fp8-global": D, "nvfp4": D // 2}[fmt]
+    n_windows = max(1, min(16, (cfg.num_rows * row_bytes_in) // out_bytes))
+
+    def bench_copy(i):
+        src = table.data_ptr() + (i % n_windows) * out_bytes
+        check_bench(blib.ple_bench_copy(src, outs[i % len(outs)].data_ptr(), out_bytes,
+                                        torch.cuda.current_stream().cuda_stream), blib)
+    bench_copy(0)
+    contig_ms = timed(bench_copy, 4 * L)
+    contig_gbps = 2 * out_bytes / (contig_ms * 1e-3) / 1e9
+    ids_rows = [ple.ple_ngram_ids(hashes[l], toks, qsl).view(-1) for l in range(L)]
+    row_copy_bytes = T * H * row_bytes_in
+    rows_of_table = table.numel() * table.element_size() // row_bytes_in
+
+    def bench_rows(i):
+        check_bench(blib.ple_bench_copy_rows(table.data_ptr(), rows_of_table, row_bytes_in,
+                                             ids_rows[i % L].data_ptr(), T * H, outs[i % len(outs)].data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream), blib)
+    bench_rows(0)
+    rows_ms = timed(bench_rows, 4 * L)
+    rows_gbps = (2 * row_copy_bytes + T * H * 4) / (rows_ms * 1e-3) / 1e9
+    del ids_rows
 
     R = b.R
     # bytes read per (token, head) row: bf16 row; fp8 codes (+ the row's scale);
@@ -249,7 +270,8 @@ def main() -> int:
         "lookup": {"kernel": "fused ids+gather" + ("" if fmt == "bf16" else f"+{fmt} dequant"),
                    "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
-                   "frac_copy_ceiling": round(lookup_gbps / copy_gbps, 4),
+                   "frac_copy_ceiling": round(lookup_gbps / rows_gbps, 4),
+                   "frac_contiguous_copy": round(lookup_gbps / contig_gbps, 4),
                    "tokens_per_s": round(T / (lookup_ms * 1e-3), 1),
                    "outputs_rotated": 8,
                    "same_output_ms": round(lookup_same_ms, 5),
@@ -261,11 +283,47 @@ def main() -> int:
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_GBps": {"gate": round(gate_bytes / (stage_ms["gate"] * 1e-3) / 1e9, 1),
                         "conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)},
-        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "copy_ceiling": {"kernel": "hand-written 16-byte streaming copy (libple_bench), one pass per wave",
+                         "random_rows_ms": round(rows_ms, 5), "random_rows_GBps": round(rows_gbps, 1),
+                         "random_rows": "the lookup's own rows (this batch's IDs, " + f"{row_bytes_in}-byte rows)",
+                         "contiguous_ms": round(contig_ms, 5), "contiguous_GBps": round(contig_gbps, 1),
+                         "bytes": out_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def bench_library():
+    """libple_bench: the streaming-copy ceilings (include/ple_bench.h)."""
+    import ctypes
+    path = os.path.join(ROOT, "layer_embedding_lookup_amd", "libple_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run python -m layer_embedding_lookup_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.ple_bench_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.ple_bench_copy_rows.argtypes = [P, I64, I32, P, I64, P, P]
+    lib.ple_bench_error_message.restype = ctypes.c_char_p
+    return lib
+
+
+def check_bench(rc, lib):
+    if rc != 0:
+        raise RuntimeError(f"libple_bench call failed ({rc}): {lib.ple_bench_error_message().decode()}")
+
+
+def host_cpu():
+    """nproc, the CPUs this process may run on, and the CPU model name."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 
 def recorded_traffic(workload):
@@ -321,11 +379,15 @@ def bench_host_table(args):
     staging = [torch.empty((T, H * D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     # the distinct-rows prefetch: layers (only hash and table are read), workspace, distinct-row count
     conv_dummy = torch.zeros((N, 4), dtype=torch.bfloat16, device=dev)
-    layers = [ple.Layer(hashes[l], tb, w_std, conv_dummy, conv_dilation=3) for l in range(L)]
+    kv_dummy = torch.zeros((2 * N, H * D), dtype=torch.bfloat16, device=dev)
+    layers = [ple.Layer(hashes[l], tb, kv_dummy, conv_dummy, conv_dilation=3) for l in range(L)]
     ws_dd = [torch.empty((ple.ple_prefetch_dedup_workspace_bytes(T, H),), dtype=torch.uint8, device=dev)
              for _ in range(2)]
     n_unique = torch.zeros((L,), dtype=torch.int32, device=dev)
     side = ple.ple_stream_create_cu_masked(args.prefetch_cus)
+    # the dedup plan's stream takes any CU: it starts once the layer's work is done, when the
+    # CUs outside the prefetch stream's mask are idle
+    plan_side = torch.cuda.Stream()
     # the layer's work runs on a non-blocking stream: the legacy null stream
     # would serialise with the (blocking) side stream and hide the overlap
     main = torch.cuda.Stream()
@@ -362,7 +424,15 @@ def bench_host_table(args):
             ple.ple_prefetch_dedup(layers[l % L], toks, qsl, staging[buf], workspace=ws_dd[buf],
                                    num_unique=n_unique[l % L:l % L + 1], stream=stream)
 
+        for buf in range(2):  # first calls load the kernels
+            fetch_dedup(0, buf, None)
+        torch.cuda.synchronize()
         dedup_ms = timed(lambda i: fetch_dedup(i, 0, None), 2 * L)
+
+        def sync_layer_dedup(i):
+            fetch_dedup(i, 0, None)
+            ple.ple_kv_proj(x_std, w_std, kv=y_std)
+        sync_dd_ms = timed(sync_layer_dedup, reps * L)
         torch.cuda.synchronize()
         unique_frac = float(n_unique.float().mean().item()) / (T * H)
 
@@ -389,6 +459,49 @@ def bench_host_table(args):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1)
 
+        def plan(l, buf, stream):
+            ple.ple_prefetch_dedup_plan(layers[l % L], toks, qsl, ws_dd[buf], stream=stream)
+
+        def fetch_planned(l, buf, stream):
+            ple.ple_prefetch_dedup_fetch(layers[l % L], T, ws_dd[buf], staging[buf],
+                                         num_unique=n_unique[l % L:l % L + 1], stream=stream)
+
+        def pipelined_split(n_layers):
+            """The dedup prefetch in two halves: the plan of layer l+2 runs on its own stream once
+            layer l's work is done, beside the fetch of layer l+1, so that no short launch of the
+            prefetch starts while the layer's work holds the CUs."""
+            ready = [torch.cuda.Event() for _ in range(2)]
+            free = [torch.cuda.Event() for _ in range(2)]
+            planned = [torch.cuda.Event() for _ in range(2)]
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(min(2, n_layers)):
+                plan_side.wait_event(e0)
+                plan(k, k, plan_side)
+                planned[k].record(plan_side)
+            side.wait_event(planned[0])
+            fetch_planned(0, 0, side)
+            ready[0].record(side)
+            for l in range(n_layers):
+                cur, nxt = l % 2, (l + 1) % 2
+                if l + 1 < n_layers:
+                    if l >= 1:
+                        side.wait_event(free[nxt])
+                    side.wait_event(planned[nxt])
+                    fetch_planned(l + 1, nxt, side)
+                    ready[nxt].record(side)
+                main.wait_event(ready[cur])
+                ple.ple_kv_proj(x_std, w_std, kv=y_std)
+                free[cur].record(main)
+                if l + 2 < n_layers:  # workspace cur is free once fetch l is done (before the layer's work)
+                    plan_side.wait_event(free[cur])
+                    plan(l + 2, cur, plan_side)
+                    planned[cur].record(plan_side)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
         def staged(n_layers):
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -404,6 +517,8 @@ def bench_host_table(args):
         pipe_ms = min(pipelined(n_layers) for _ in range(3))
         pipelined(L, fetch_dedup)
         pipe_dd_ms = min(pipelined(n_layers, fetch_dedup) for _ in range(3))
+        pipelined_split(L)
+        pipe_split_ms = min(pipelined_split(n_layers) for _ in range(3))
         staged_ms = min(staged(n_layers) for _ in range(3))
     finally:
         torch.cuda.synchronize()
@@ -433,8 +548,12 @@ def bench_host_table(args):
                   "host_bytes_per_layer": int(round(unique_frac * rows_bytes)),
                   "lookup_ms_sync": round(dedup_ms, 4),
                   "host_link_GBps": round(unique_frac * rows_bytes / (dedup_ms * 1e-3) / 1e9, 2),
+                  "sync_ms_per_layer": round(sync_dd_ms, 4),
                   "pipelined_ms_per_layer": round(pipe_dd_ms / n_layers, 4),
-                  "exposed_lookup_ms_per_layer": round((pipe_dd_ms - staged_ms) / n_layers, 4)},
+                  "exposed_lookup_ms_per_layer": round((pipe_dd_ms - staged_ms) / n_layers, 4),
+                  "split": {"entry_points": "ple_prefetch_dedup_plan on a second stream, ple_prefetch_dedup_fetch",
+                            "pipelined_ms_per_layer": round(pipe_split_ms / n_layers, 4),
+                            "exposed_lookup_ms_per_layer": round((pipe_split_ms - staged_ms) / n_layers, 4)}},
     }
     print(json.dumps(line), flush=True)
     hb.close()
@@ -737,30 +856,66 @@ def bench_spec_decode(args):
 
 
 def cpu_baseline(cfg, b, table_h, scales_h, kvw_h, conv_w_h, hidden_h, n_tokens, workload):
-    """The oracle, single-threaded, on a bounded sample: the first n_tokens of
-    the batch (whole requests, the last one cut to a prefix chunk; by causality
-    their outputs equal the full batch's) through the whole path."""
+    """The oracle, single-threaded and pinned to one core of the host: its IDs and
+    row gather (+ dequant) over every token of the batch, and the whole path
+    (ids, gather, kv_proj, gate, conv) on a bounded sample, the first n_tokens
+    of the batch (whole requests, the last one cut to a prefix chunk; by
+    causality their outputs equal the full batch's)."""
     import numpy as np
 
     import oracle
     import workloads as wl
 
-    n = int(min(n_tokens, cfg.T))
-    q = b.qsl.astype(np.int64)
-    R = int(np.searchsorted(q, n, side="left"))  # requests 0..R-1 cover [0, n)
-    qsl = np.minimum(q[:R + 1], n).astype(np.int32)
-    qsl[-1] = n
-    log(f"cpu baseline: oracle on the first {n} tokens ({R} requests), whole path")
-    ids_args = dict(input_ids=b.input_ids[:n], qsl=qsl, multipliers=b.multipliers[0],
-                    vocab_sizes=b.vocab_sizes, offsets=b.offsets, context_len=cfg.context_len,
-                    heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS)
-    t0 = time.perf_counter()
-    oracle.prefill(ids_args, table_h, scales_h, hidden_h[:n], kvw_h, conv_w_h, cfg.conv_dilation, qsl=qsl,
-                   eps=cfg.eps)
-    dt = time.perf_counter() - t0
+    host = host_cpu()
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        T, H, D = cfg.T, cfg.H, cfg.D
+        ids_args_all = dict(input_ids=b.input_ids, qsl=b.qsl, multipliers=b.multipliers[0],
+                            vocab_sizes=b.vocab_sizes, offsets=b.offsets, context_len=cfg.context_len,
+                            heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS)
+        log(f"cpu baseline: oracle pinned to core {core}: ids + gather over all {T} tokens")
+        t0 = time.perf_counter()
+        ids = oracle.ngram_ids(**ids_args_all)
+        if scales_h is None:
+            oracle.gather_bf16(table_h, ids)
+        elif isinstance(scales_h, tuple):
+            oracle.gather_nvfp4(table_h, scales_h[0], scales_h[1], ids)
+        elif np.size(scales_h) == 1:
+            oracle.gather_fp8_global(table_h, np.asarray(scales_h).reshape(-1)[0], ids)
+        else:
+            oracle.gather_fp8(table_h, scales_h, ids)
+        dt_ig = time.perf_counter() - t0
+        if scales_h is None:
+            row_read = D * 2
+        elif isinstance(scales_h, tuple):
+            row_read = D // 2 + D // 16
+        else:
+            row_read = D if np.size(scales_h) == 1 else D + 4
+        ig_bytes = T * H * (row_read + D * 2) + T * 4 + (b.R + 1) * 4
+
+        n = int(min(n_tokens, cfg.T))
+        q = b.qsl.astype(np.int64)
+        R = int(np.searchsorted(q, n, side="left"))  # requests 0..R-1 cover [0, n)
+        qsl = np.minimum(q[:R + 1], n).astype(np.int32)
+        qsl[-1] = n
+        log(f"cpu baseline: oracle on the first {n} tokens ({R} requests), whole path")
+        ids_args = dict(ids_args_all, input_ids=b.input_ids[:n], qsl=qsl)
+        t0 = time.perf_counter()
+        oracle.prefill(ids_args, table_h, scales_h, hidden_h[:n], kvw_h, conv_w_h, cfg.conv_dilation, qsl=qsl,
+                       eps=cfg.eps)
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, allowed)
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} tokens ({R} requests) of the {workload} batch, whole path "
-                      f"(ids, gather, kv_proj, gate, conv), single-threaded C, {dt:.1f} s"}
+                      f"(ids, gather, kv_proj, gate, conv), single-threaded C pinned to one core, {dt:.1f} s",
+            "ids_gather": {"tokens": T, "s": round(dt_ig, 3), "tokens_per_s": round(T / dt_ig, 1),
+                           "GBps": round(ig_bytes / dt_ig / 1e9, 3),
+                           "what": "ids + row gather (+ dequant) over every token, same algorithmic bytes as "
+                                   "the GPU lookup"},
+            "host": host}
 
 
 if __name__ == "__main__":

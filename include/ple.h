@@ -201,14 +201,38 @@ int ple_prefetch(const ple_layer_desc* layer, const ple_batch_desc* batch, uint1
  * device memory from their first read instead of crossing the host link
  * again.  Same result as ple_prefetch, bit for bit.
  * workspace: device memory of ple_prefetch_dedup_workspace_bytes(T, H) bytes,
- * 256-byte aligned (IDs, a hash set and the repeat map; not read before being
- * written).  num_unique: device int32 receiving the number of distinct rows
+ * 256-byte aligned (IDs, a hash set, the list of distinct rows and the repeat
+ * map; cleared or written before being read).  num_unique: device int32 receiving the number of distinct rows
  * (the rows read from the table), or NULL.  T*H at most 2^22
  * (PLE_ERR_UNSUPPORTED beyond; the size function then returns 0).
  */
 int ple_prefetch_dedup(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging,
                        void* workspace, size_t workspace_bytes, int32_t* num_unique, void* stream);
 size_t ple_prefetch_dedup_workspace_bytes(int64_t max_tokens, int32_t num_heads);
+
+/*
+ * ple_prefetch_dedup in two calls, the first then the second on one stream
+ * ([P2] 功能与动机: the prefetch hides the host-link read behind the layer's
+ * work).  A caller that overlaps the prefetch with other kernels can plan the
+ * next layer while the current fetch runs, so that the plan's short launches
+ * do not queue behind those kernels.
+ * ple_prefetch_dedup_plan: the row IDs of every (token, head), the hash set of
+ *   distinct IDs and the list of their first positions, into workspace (as
+ *   for ple_prefetch_dedup, sized by ple_prefetch_dedup_workspace_bytes);
+ *   also writes batch->ngram_context_out when given.  No staging.
+ * ple_prefetch_dedup_fetch: reads the listed rows from the table into
+ *   staging (device bf16 [T][H*D]) and copies each repeated row from its first
+ *   read; num_unique as for ple_prefetch_dedup.  It takes the same layer
+ *   table and num_heads, num_tokens = the plan's batch->num_tokens, and the
+ *   workspace the plan filled, unchanged in between; the caller orders the
+ *   fetch after the plan (same stream, or an event).
+ * Errors as for ple_prefetch_dedup; T == 0 launches nothing except the
+ * context output (plan) and the zero count (fetch with num_unique).
+ */
+int ple_prefetch_dedup_plan(const ple_layer_desc* layer, const ple_batch_desc* batch, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int ple_prefetch_dedup_fetch(const ple_layer_desc* layer, int64_t num_tokens, void* workspace,
+                             size_t workspace_bytes, uint16_t* staging, int32_t* num_unique, void* stream);
 
 /*
  * Merged key/value projection ([P3] 实现拆解 item 1):

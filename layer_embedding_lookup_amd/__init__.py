@@ -27,7 +27,8 @@ from .capi import (PLE_DTYPE_BF16, PLE_DTYPE_FP8_E4M3, PLE_DTYPE_FP8_E4M3_GLOBAL
                    PLE_ERR_UNSUPPORTED, PLE_ERR_WORKSPACE, PLE_MAX_CONTEXT, PLE_MAX_HEADS, PLE_OK)
 
 __all__ = ["HashParams", "Table", "Layer", "ple_ngram_ids", "ple_gather", "ple_lookup", "ple_prefetch",
-           "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes", "ple_dp_gather_slot", "ple_head_shard",
+           "ple_prefetch_dedup", "ple_prefetch_dedup_workspace_bytes", "ple_prefetch_dedup_plan",
+           "ple_prefetch_dedup_fetch", "ple_dp_gather_slot", "ple_head_shard",
            "ple_select_rows",
            "ple_kv_proj", "ple_gate", "ple_conv", "ple_spec_commit", "ple_prefill_fused", "ple_prefill_workspace_bytes",
            "ple_prefill_fused_noalloc",
@@ -296,6 +297,35 @@ def ple_prefetch_dedup(layer: Layer, input_ids, query_start_loc, staging, *, wor
     capi.check(capi.load().ple_prefetch_dedup(ctypes.byref(L), ctypes.byref(b), _ptr(staging), _ptr(workspace),
                                               _nbytes(workspace), _ptr(num_unique), _stream(stream)),
                "ple_prefetch_dedup")
+    return staging
+
+
+def ple_prefetch_dedup_plan(layer: Layer, input_ids, query_start_loc, workspace, *, ngram_context=None,
+                            ngram_context_out=None, stream=None):
+    """The first half of ple_prefetch_dedup: IDs, distinct-ID set and list into workspace."""
+    _req("input_ids", input_ids, (None,), _I32)
+    T = input_ids.shape[0]
+    _req_bytes("workspace", workspace, ple_prefetch_dedup_workspace_bytes(T, layer.hash.num_heads))
+    L = layer.desc()
+    b = _batch(input_ids, query_start_loc, ngram_context, ngram_context_out, context_len=layer.hash.context_len)
+    _same_device(input_ids, workspace)
+    capi.check(capi.load().ple_prefetch_dedup_plan(ctypes.byref(L), ctypes.byref(b), _ptr(workspace),
+                                                   _nbytes(workspace), _stream(stream)), "ple_prefetch_dedup_plan")
+    return workspace
+
+
+def ple_prefetch_dedup_fetch(layer: Layer, num_tokens: int, workspace, staging, *, num_unique=None, stream=None):
+    """The second half of ple_prefetch_dedup: the listed rows into staging, then the repeats;
+    workspace as the plan for num_tokens tokens left it."""
+    T = int(num_tokens)
+    _req("staging", staging, (T, layer.hash.num_heads * layer.table.dim), _BF16)
+    _req("num_unique", num_unique, (1,), _I32, optional=True)
+    _req_bytes("workspace", workspace, ple_prefetch_dedup_workspace_bytes(T, layer.hash.num_heads))
+    L = layer.desc()
+    _same_device(staging, num_unique, workspace)
+    capi.check(capi.load().ple_prefetch_dedup_fetch(ctypes.byref(L), T, _ptr(workspace), _nbytes(workspace),
+                                                    _ptr(staging), _ptr(num_unique), _stream(stream)),
+               "ple_prefetch_dedup_fetch")
     return staging
 
 

@@ -1,4 +1,5 @@
-"""Builds libple.so (hand-written HIP kernels + C ABI) for gfx950 with hipcc.
+"""Builds libple.so (hand-written HIP kernels + C ABI) for gfx950 with hipcc, and
+libple_bench.so (the benchmark's streaming-copy ceilings).
 
 Usage: python -m layer_embedding_lookup_amd.build   (or call build()).
 The library is built in-tree next to this file.
@@ -16,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libple.so")
+# the benchmark's streaming-copy ceilings (include/ple_bench.h), a library of their own
+BENCH_LIB = os.path.join(HERE, "libple_bench.so")
+BENCH_SOURCE = "ple_bench.hip"
 SOURCES = ["ple_api.cpp", "ple_lookup.hip", "ple_kv_proj.hip", "ple_gate_conv.hip", "ple_dedup.hip", "ple_dp.hip",
            "ple_spec.hip", "ple_static.hip"]
 ARCH = "gfx950"
@@ -40,7 +44,9 @@ def build(force: bool = True, verbose: bool = False, jobs: int = 4) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     deps = srcs + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")] + \
         [os.path.join(INCLUDE, "ple.h")]
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(os.path.getmtime(d) for d in deps):
+    deps.append(os.path.join(CSRC, BENCH_SOURCE))
+    if not force and all(os.path.exists(lb) and os.path.getmtime(lb) >= max(os.path.getmtime(d) for d in deps)
+                         for lb in (LIB, BENCH_LIB)):
         return LIB
     cc = hipcc()
     objdir = os.path.join(ROOT, "_build", "libple")
@@ -58,12 +64,13 @@ def build(force: bool = True, verbose: bool = False, jobs: int = 4) -> str:
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (BENCH_LIB, [compile_one(os.path.join(CSRC, BENCH_SOURCE))])):
+        tmp = lib + f".tmp{os.getpid()}"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc link failed:\n{res.stdout}\n{res.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -64,6 +64,9 @@ _PROTOS = {
     "ple_prefetch_dedup": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P, P,
                                           ctypes.c_size_t, P, P]),
     "ple_prefetch_dedup_workspace_bytes": (ctypes.c_size_t, [I64, I32]),
+    "ple_prefetch_dedup_plan": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), ctypes.POINTER(ple_batch_desc), P,
+                                               ctypes.c_size_t, P]),
+    "ple_prefetch_dedup_fetch": (ctypes.c_int, [ctypes.POINTER(ple_layer_desc), I64, P, ctypes.c_size_t, P, P, P]),
     "ple_dp_gather_slot": (ctypes.c_int, [P, I32, I32, I32, P, P]),
     "ple_head_shard": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P]),
     "ple_select_rows": (ctypes.c_int, [P, I32, I64, I32, I64, I32, P, P]),

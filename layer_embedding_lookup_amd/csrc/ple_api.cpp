@@ -390,6 +390,60 @@ int dedup_log2cap(int64_t n) {
     while (((int64_t)1 << l) < 2 * n) ++l;
     return l;
 }
+
+// The workspace of n = T*H positions: ids, slot_of, list (distinct) and
+// repeats [n], the two lists' counts, keys and rep [cap].
+struct DedupWorkspace {
+    int log2cap;
+    size_t cap;
+    int32_t* ids;
+    int32_t* slot_of;
+    int32_t* list;
+    int32_t* repeats;
+    int32_t* counts;  // [0] distinct positions, [1] repeats
+    int32_t* keys;
+    int32_t* rep;
+};
+
+DedupWorkspace dedup_workspace(void* workspace, int64_t n) {
+    DedupWorkspace w;
+    w.log2cap = dedup_log2cap(n);
+    w.cap = (size_t)1 << w.log2cap;
+    const size_t nb = round256((size_t)n * 4);
+    char* ws = (char*)workspace;
+    w.ids = (int32_t*)ws;
+    w.slot_of = (int32_t*)(ws + nb);
+    w.list = (int32_t*)(ws + 2 * nb);
+    w.repeats = (int32_t*)(ws + 3 * nb);
+    w.counts = (int32_t*)(ws + 4 * nb);
+    w.keys = (int32_t*)(ws + 4 * nb + 256);
+    w.rep = (int32_t*)(ws + 4 * nb + 256 + round256(w.cap * 4));
+    return w;
+}
+
+// Checks shared by the plan and the fetch: the layer's hash and table, the
+// row limit and the workspace (needed when T > 0).
+int dedup_checks(const ple_layer_desc* layer, int64_t T, const void* workspace, size_t workspace_bytes,
+                 HashParams* hp, int* cpr_log2) {
+    if (layer == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
+    int rc = validate_hash(&layer->hash, hp);
+    if (rc) return rc;
+    rc = validate_table(&layer->table, cpr_log2);
+    if (rc) return rc;
+    rc = validate_heads_in_table(&layer->hash, &layer->table);
+    if (rc) return rc;
+    if (T < 0 || T > PLE_MAX_TOKENS)
+        return fail(PLE_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 0..%d", (long long)T, PLE_MAX_TOKENS);
+    const int64_t n = T * layer->hash.num_heads;
+    if (n > kDedupMaxRows)
+        return fail(PLE_ERR_UNSUPPORTED, "dedup prefetch takes at most %lld rows (T*H = %lld)",
+                    (long long)kDedupMaxRows, (long long)n);
+    const size_t need = ple_prefetch_dedup_workspace_bytes(T, layer->hash.num_heads);
+    if (T > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need))
+        return fail(PLE_ERR_WORKSPACE, "dedup workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    return PLE_OK;
+}
 }  // namespace
 
 size_t ple_prefetch_dedup_workspace_bytes(int64_t max_tokens, int32_t num_heads) {
@@ -397,66 +451,103 @@ size_t ple_prefetch_dedup_workspace_bytes(int64_t max_tokens, int32_t num_heads)
     const int64_t n = max_tokens * num_heads;
     if (n > kDedupMaxRows) return 0;
     const size_t cap = (size_t)1 << dedup_log2cap(n);
-    return 2 * round256((size_t)n * 4) + 2 * round256(cap * 4);
+    // ids, slot_of, list and repeats [n], the lists' counts, keys and rep [cap]
+    return 4 * round256((size_t)n * 4) + 256 + 2 * round256(cap * 4);
 }
 
-int ple_prefetch_dedup(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging,
-                       void* workspace, size_t workspace_bytes, int32_t* num_unique, void* stream) {
-    if (layer == nullptr) return fail(PLE_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
-    const ple_hash_desc* hash = &layer->hash;
-    const ple_table_desc* table = &layer->table;
+int ple_prefetch_dedup_plan(const ple_layer_desc* layer, const ple_batch_desc* batch, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     HashParams hp;
     int cpr_log2 = -1;
-    int rc = validate_hash(hash, &hp);
+    int rc = validate_batch_tokens(batch);
     if (rc) return rc;
-    rc = validate_table(table, &cpr_log2);
-    if (rc) return rc;
-    rc = validate_heads_in_table(hash, table);
-    if (rc) return rc;
-    rc = validate_batch_tokens(batch);
+    rc = dedup_checks(layer, batch->num_tokens, workspace, workspace_bytes, &hp, &cpr_log2);
     if (rc) return rc;
     const int64_t T = batch->num_tokens;
-    const int H = hash->num_heads;
-    const int64_t n = T * H;
-    if (n > kDedupMaxRows)
-        return fail(PLE_ERR_UNSUPPORTED, "dedup prefetch takes at most %lld rows (T*H = %lld)",
-                    (long long)kDedupMaxRows, (long long)n);
-    if (T > 0 && (staging == nullptr || !aligned16(staging)))
-        return fail(PLE_ERR_INVALID_ARGUMENT, "staging is NULL or not 16-byte aligned");
-    if (num_unique != nullptr && !aligned4(num_unique)) return fail(PLE_ERR_INVALID_ARGUMENT, "num_unique misaligned");
-    const size_t need = ple_prefetch_dedup_workspace_bytes(T, H);
-    if (T > 0 && (workspace == nullptr || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need))
-        return fail(PLE_ERR_WORKSPACE, "dedup workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                    workspace_bytes);
-    if (T == 0 && num_unique == nullptr && (batch->ngram_context_out == nullptr || batch->num_reqs == 0)) return ok();
+    if (T == 0 && (batch->ngram_context_out == nullptr || batch->num_reqs == 0)) return ok();
     rc = check_device();
     if (rc) return rc;
     hipStream_t s = (hipStream_t)stream;
     if (T > 0) {
-        const int l2 = dedup_log2cap(n);
-        char* ws = (char*)workspace;
-        int32_t* ids = (int32_t*)ws;
-        int32_t* slot_rep = (int32_t*)(ws + round256((size_t)n * 4));
-        int32_t* keys = (int32_t*)(ws + 2 * round256((size_t)n * 4));
-        int32_t* rep = (int32_t*)(ws + 2 * round256((size_t)n * 4) + round256(((size_t)1 << l2) * 4));
+        const int64_t n = T * layer->hash.num_heads;
+        const DedupWorkspace w = dedup_workspace(workspace, n);
+        // IDs, with the hash set's keys and the lists' counts cleared by the same launch
         hipError_t e = launch_ngram_ids(hp, batch->input_ids, batch->query_start_loc, T, batch->num_reqs,
-                                        batch->ngram_context, ids, s);
-        if (e == hipSuccess) e = launch_dedup(ids, n, keys, rep, l2, slot_rep, num_unique, s);
-        if (e == hipSuccess) {
-            HashParams none;
-            memset(&none, 0, sizeof(none));
-            LookupArgs g = lookup_args(table, H, cpr_log2, nullptr, ids, T, nullptr, staging);
-            g.rep_of = slot_rep;
-            e = launch_lookup(none, g, table->dtype, kModeIds, s);
-        }
-        if (e == hipSuccess) e = launch_dedup_copy(slot_rep, n, table->dim, staging, s);
-        if (e != hipSuccess) return hip_fail(e, "dedup prefetch launch");
-    } else if (num_unique != nullptr) {
-        hipError_t e = launch_dedup(nullptr, 0, nullptr, nullptr, 8, nullptr, num_unique, s);
-        if (e != hipSuccess) return hip_fail(e, "dedup prefetch launch");
+                                        batch->ngram_context, w.ids, s, w.keys, (int64_t)w.cap, w.counts, 2);
+        if (e == hipSuccess)
+            e = launch_dedup_insert(w.ids, n, w.keys, w.rep, w.log2cap, w.slot_of, w.list, w.repeats, w.counts, s);
+        if (e != hipSuccess) return hip_fail(e, "dedup plan launch");
     }
-    rc = run_context_out(hash, batch, s);
+    rc = run_context_out(&layer->hash, batch, s);
     return rc ? rc : ok();
+}
+
+int ple_prefetch_dedup_fetch(const ple_layer_desc* layer, int64_t num_tokens, void* workspace,
+                             size_t workspace_bytes, uint16_t* staging, int32_t* num_unique, void* stream) {
+    HashParams hp;
+    int cpr_log2 = -1;
+    int rc = dedup_checks(layer, num_tokens, workspace, workspace_bytes, &hp, &cpr_log2);
+    if (rc) return rc;
+    const int64_t T = num_tokens;
+    if (T > 0 && (staging == nullptr || !aligned16(staging)))
+        return fail(PLE_ERR_INVALID_ARGUMENT, "staging is NULL or not 16-byte aligned");
+    if (num_unique != nullptr && !aligned4(num_unique)) return fail(PLE_ERR_INVALID_ARGUMENT, "num_unique misaligned");
+    if (T == 0 && num_unique == nullptr) return ok();
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const ple_table_desc* table = &layer->table;
+    hipError_t e;
+    if (T > 0) {
+        const int64_t n = T * layer->hash.num_heads;
+        const DedupWorkspace w = dedup_workspace(workspace, n);
+        // the distinct rows from the table: one "token" per list entry, one head
+        HashParams none;
+        memset(&none, 0, sizeof(none));
+        LookupArgs g = lookup_args(table, 1, cpr_log2, nullptr, w.ids, n, nullptr, staging);
+        g.list = w.list;
+        g.list_count = w.counts;
+        g.count_out = num_unique;
+        e = launch_lookup(none, g, table->dtype, kModeList, s);
+        if (e == hipSuccess) {
+            // then each repeat from its first read: the same walk over the
+            // repeats, with the staging rows as a bf16 table of n rows and
+            // row rep[slot_of[i]] for position i
+            ple_table_desc st;
+            memset(&st, 0, sizeof(st));
+            st.table = staging;
+            st.num_rows = n;
+            st.dim = table->dim;
+            st.dtype = PLE_DTYPE_BF16;
+            LookupArgs c = lookup_args(&st, 1, cpr_log2, nullptr, w.slot_of, n, nullptr, staging);
+            c.list = w.repeats;
+            c.list_count = w.counts + 1;
+            c.rep = w.rep;
+            c.rep_len = (int64_t)w.cap;
+            e = launch_lookup(none, c, PLE_DTYPE_BF16, kModeList, s);
+        }
+    } else {
+        // nothing to look up: report zero distinct rows
+        e = launch_dedup_count(nullptr, num_unique, s);
+    }
+    return e == hipSuccess ? ok() : hip_fail(e, "dedup fetch launch");
+}
+
+int ple_prefetch_dedup(const ple_layer_desc* layer, const ple_batch_desc* batch, uint16_t* staging,
+                       void* workspace, size_t workspace_bytes, int32_t* num_unique, void* stream) {
+    HashParams hp;
+    int cpr_log2 = -1;
+    int rc = validate_batch_tokens(batch);
+    if (rc) return rc;
+    // every check of both calls before either launches
+    rc = dedup_checks(layer, batch->num_tokens, workspace, workspace_bytes, &hp, &cpr_log2);
+    if (rc) return rc;
+    if (batch->num_tokens > 0 && (staging == nullptr || !aligned16(staging)))
+        return fail(PLE_ERR_INVALID_ARGUMENT, "staging is NULL or not 16-byte aligned");
+    if (num_unique != nullptr && !aligned4(num_unique)) return fail(PLE_ERR_INVALID_ARGUMENT, "num_unique misaligned");
+    rc = ple_prefetch_dedup_plan(layer, batch, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return ple_prefetch_dedup_fetch(layer, batch->num_tokens, workspace, workspace_bytes, staging, num_unique, stream);
 }
 
 int ple_dp_gather_slot(const int64_t* token_counts, int32_t dp_size, int32_t group_size, int32_t dp_rank,

@@ -5,14 +5,23 @@
 
 namespace ple {
 
-enum { kModeHash = 0, kModeIds = 1 };
+// How the lookup kernel gets its row IDs: hashed from the tokens, read from
+// caller IDs [T][H], or (list) for k below a device-side count, row
+// ids_in[list[k]] (or, with rep, row rep[ids_in[list[k]]]) written to output
+// row list[k] (the distinct rows of the deduplicating prefetch, then its
+// repeats copied within the output)
+enum { kModeHash = 0, kModeIds = 1, kModeList = 2 };
 
 struct LookupArgs {
     const int32_t* tok;
     const int32_t* qsl;
     const int32_t* ctx;
     const int32_t* ids_in;
-    const int32_t* rep_of;  // ids mode, optional: position i is gathered only when rep_of[i] == i
+    const int32_t* list;        // list mode: positions into ids_in / output rows
+    const int32_t* list_count;  // list mode: device count of list entries (at most num_tokens)
+    const int32_t* rep;         // list mode, optional: row = rep[ids_in[...]], rep has rep_len entries
+    int64_t rep_len;
+    int32_t* count_out;         // list mode, optional: receives *list_count
     int32_t* ids_out;
     const void* table;
     const float* scales;          // fp8: per-row scales (scale_stride 1) or one scale (0); NVFP4: one scale
@@ -31,16 +40,24 @@ struct LookupArgs {
 // kernel-side table formats (the fp8 per-row and global-scale tables share one kernel)
 enum { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 3 };
 
+// IDs [T][H]; extra blocks of the same launch set clear[0 .. clear_n) to -1
+// and zero[0 .. zero_n) to 0 when those are non-NULL (zero_n at most 64).
 hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int32_t* qsl, int64_t T, int R,
-                            const int32_t* ctx, int32_t* ids, hipStream_t s);
+                            const int32_t* ctx, int32_t* ids, hipStream_t s, int32_t* clear = nullptr,
+                            int64_t clear_n = 0, int32_t* zero = nullptr, int zero_n = 0);
 hipError_t launch_context_out(const int32_t* tok, const int32_t* qsl, int64_t T, int R, int C, int32_t eos,
                               const int32_t* ctx, int32_t* ctx_out, hipStream_t s);
 int lookup_tokens_per_wave(int H, int chunks_per_row, int dtype, int64_t num_tokens);
 hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s);
 
-hipError_t launch_dedup(const int32_t* ids, int64_t n, int32_t* keys, int32_t* rep, int log2cap,
-                        int32_t* slot_rep, int32_t* num_unique, hipStream_t s);
-hipError_t launch_dedup_copy(const int32_t* rep_of, int64_t n, int dim, uint16_t* rows, hipStream_t s);
+// Distinct rows of ids [n] (keys and counts cleared beforehand): slot_of[i]
+// = the hash-set slot of position i's ID, rep[slot] = the position whose row
+// fills it, list[0 .. counts[0]) = those positions (one per distinct ID),
+// repeats[0 .. counts[1]) = every other position.
+hipError_t launch_dedup_insert(const int32_t* ids, int64_t n, int32_t* keys, int32_t* rep, int log2cap,
+                               int32_t* slot_of, int32_t* list, int32_t* repeats, int32_t* counts, hipStream_t s);
+// *num_unique = *count (0 when count is NULL), one thread.
+hipError_t launch_dedup_count(const int32_t* count, int32_t* num_unique, hipStream_t s);
 
 hipError_t launch_select_rows(const uint16_t* gathered, int E, int64_t slot, int rank, int64_t n, int width,
                               uint16_t* out, hipStream_t s);

@@ -258,7 +258,7 @@ __device__ __forceinline__ void store16(u32x4* p, u32x4 v, bool nt) {
 // bf16 tables take this stream by default: for plain row copies it measured
 // faster than the scalar-address stream below.
 template <int DTYPE, int MODE, int UNROLL>
-__device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const StreamArgs& a, int id, int skip,
+__device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const StreamArgs& a, int id, int orow,
                                                  float tscale, int lane) {
     constexpr int IB = in_bytes<DTYPE>();
     const int64_t row_bytes = (int64_t)a.cpr * IB;
@@ -276,8 +276,7 @@ __device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const Stre
             row = row < a.nrows ? row : a.nrows - 1;
             const int rid = __shfl(id, row, kWave);
             if (DTYPE == kFmtFP8) sc[u] = __shfl(scale, row, kWave);
-            const int rskip = MODE == kModeIds ? __shfl(skip, row, kWave) : 0;
-            if (idx < a.total && !rskip) {
+            if (idx < a.total) {
                 const int ch = idx - row * a.cpr;
                 const char* src = a.table + (int64_t)rid * row_bytes + (int64_t)ch * IB;
                 if (DTYPE == kFmtBF16) {
@@ -294,18 +293,20 @@ __device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const Stre
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int idx = base + u * kWave + lane;
-            int rskip = 0;
-            if (MODE == kModeIds) {
-                const int row = a.shift >= 0 ? (idx >> a.shift) : (idx / a.cpr);
-                rskip = __shfl(skip, row < a.nrows ? row : a.nrows - 1, kWave);
-            }
-            if (idx < a.total && !rskip) {
+            if (idx < a.total) {
+                // list mode: each row goes to its own output row (list entry)
+                u32x4* dst = out + idx;
+                if (MODE == kModeList) {
+                    int row = a.shift >= 0 ? (idx >> a.shift) : (idx / a.cpr);
+                    row = row < a.nrows ? row : a.nrows - 1;
+                    dst = (u32x4*)g.rows + (int64_t)__shfl(orow, row, kWave) * a.cpr + (idx - row * a.cpr);
+                }
                 if (DTYPE == kFmtBF16)
-                    store16(out + idx, v[u], PLE_LOOKUP_NT_STORE_BF16);
+                    store16(dst, v[u], PLE_LOOKUP_NT_STORE_BF16);
                 else if (DTYPE == kFmtFP8)
-                    store16(out + idx, dequant8_fp8(v[u].x, v[u].y, sc[u]), PLE_LOOKUP_NT_STORE_QUANT);
+                    store16(dst, dequant8_fp8(v[u].x, v[u].y, sc[u]), PLE_LOOKUP_NT_STORE_QUANT);
                 else
-                    store16(out + idx, dequant8_fp4(v[u].x, bsc[u], tscale), PLE_LOOKUP_NT_STORE_QUANT);
+                    store16(dst, dequant8_fp4(v[u].x, bsc[u], tscale), PLE_LOOKUP_NT_STORE_QUANT);
             }
         }
     }
@@ -318,11 +319,11 @@ __device__ __forceinline__ void stream_rows_lane(const LookupArgs& g, const Stre
 // load then takes them by lane reads into scalar registers, so the loads go
 // out back to back from scalar bases.  The wave's output slab is a buffer
 // resource: a store at an offset past its end is dropped by the hardware,
-// which masks the ragged tail and the skipped rows without a branch (a
-// branch around each store lets the compiler sink the loads into it).
-template <int DTYPE, int MODE, int UNROLL>
-__device__ __forceinline__ void stream_rows_scalar(const LookupArgs& g, const StreamArgs& a, int id, int skip,
-                                                   float tscale, int lane) {
+// which masks the ragged tail without a branch (a branch around each store
+// lets the compiler sink the loads into it).
+template <int DTYPE, int UNROLL>
+__device__ __forceinline__ void stream_rows_scalar(const LookupArgs& g, const StreamArgs& a, int id, float tscale,
+                                                   int lane) {
     constexpr int IB = in_bytes<DTYPE>();
     const int64_t row_bytes = (int64_t)a.cpr * IB;
     const __amdgpu_buffer_rsrc_t orsrc =
@@ -343,8 +344,7 @@ __device__ __forceinline__ void stream_rows_scalar(const LookupArgs& g, const St
         const int pcp = P & ((1 << lppr) - 1);
         const int prowc = prow < a.nrows ? prow : a.nrows - 1;
         const uint64_t paddr = shfl64(my_row, prowc) + (uint64_t)(pcp * kWave * IB);
-        const int pskip = MODE == kModeIds ? __shfl(skip, prowc, kWave) : 0;
-        const int psoff = (prow < a.nrows && !pskip) ? (prow * a.cpr + pcp * kWave) * 16 : a.total * 16;
+        const int psoff = prow < a.nrows ? (prow * a.cpr + pcp * kWave) * 16 : a.total * 16;
         uint64_t pbs = 0;
         if (DTYPE == kFmtNVFP4) pbs = shfl64(my_bs, prowc) + (uint64_t)(pcp * kWave / 2);
         u32x4 v[UNROLL];
@@ -354,9 +354,7 @@ __device__ __forceinline__ void stream_rows_scalar(const LookupArgs& g, const St
         for (int u = 0; u < UNROLL; ++u) {
             soff[u] = __builtin_amdgcn_readlane(psoff, u);
             rsel[u] = DTYPE == kFmtFP8 ? __builtin_amdgcn_readlane(prowc, u) : 0;
-            // computed IDs always load (the address is a valid row); caller IDs
-            // skip the repeated rows
-            if (MODE == kModeHash || soff[u] < a.total * 16) {
+            {  // every pass loads (the address is a valid row); stores past the slab are dropped
                 const uint64_t rb = readlane64(paddr, u);
                 if (DTYPE == kFmtBF16) {
                     v[u] = __builtin_nontemporal_load((gptr<u32x4>)rb + lane);
@@ -381,7 +379,12 @@ __device__ __forceinline__ void stream_rows_scalar(const LookupArgs& g, const St
             } else {
                 o = dequant8_fp4(v[u].x, bsc[u], tscale);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, lane * 16, soff[u], nt ? 2 : 0);
+            // the whole offset in the vector operand, soffset the constant 0:
+            // with a register soffset the compiler takes a 128-bit buffer
+            // store as free of the store-data hazard and may overwrite the
+            // data registers with the very next VALU instruction, which
+            // corrupted stored dwords now and then (dequantizing formats)
+            __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, lane * 16 + soff[u], 0, nt ? 2 : 0);
         }
     }
 }
@@ -426,21 +429,39 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
         wave_find_request_probed(g.qsl, qp, g.num_reqs, t, t0, nt, my_k, lane, r, a);
         id = window_id(in, hp.context_len, hp.eos, g.ctx, r, a, t);
         if (active && g.ids_out != nullptr) g.ids_out[t0 * H + lane] = id;
-    } else {
+    } else if (MODE == kModeIds) {
         id = active ? g.ids_in[t0 * H + lane] : 0;
         id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
     }
+    // list mode (one head: a "token" is a list entry): entries at or past the
+    // device-side count are left alone
+    int orow = 0;
+    int nrows_l = nrows;
+    if (MODE == kModeList) {
+        int cnt = *g.list_count;
+        cnt = cnt < 0 ? 0 : (cnt > g.num_tokens ? (int)g.num_tokens : cnt);
+        if (g.count_out != nullptr && wave == 0 && lane == 0) *g.count_out = cnt;
+        if (t0 >= cnt) return;  // whole wave (no barriers in this mode)
+        nrows_l = (int)min((int64_t)nrows, cnt - t0);
+        if (lane < nrows_l) {
+            orow = g.list[t0 + lane];
+            orow = orow < 0 ? 0 : (orow >= g.num_tokens ? (int)(g.num_tokens - 1) : orow);
+            id = g.ids_in[orow];
+            if (g.rep != nullptr) {
+                id = id < 0 ? 0 : (id >= g.rep_len ? (int32_t)(g.rep_len - 1) : id);
+                id = g.rep[id];
+            }
+            id = id < 0 ? 0 : (id >= g.num_rows ? (int32_t)(g.num_rows - 1) : id);
+        }
+    }
     if (!live) return;  // whole wave
-    // ids mode with rep_of: a repeated row is left for a later copy
-    int skip = 0;
-    if (MODE == kModeIds && g.rep_of != nullptr && active) skip = g.rep_of[t0 * H + lane] != (int32_t)(t0 * H + lane);
     const float tscale = DTYPE == kFmtNVFP4 ? g.scales[0] : 0.f;
 
-    const StreamArgs sa = stream_args(g, t0, nrows);
+    const StreamArgs sa = stream_args(g, t0, nrows_l);
     if (SCALAR_ROWS)
-        stream_rows_scalar<DTYPE, MODE, UNROLL>(g, sa, id, skip, tscale, lane);
+        stream_rows_scalar<DTYPE, UNROLL>(g, sa, id, tscale, lane);
     else
-        stream_rows_lane<DTYPE, MODE, UNROLL>(g, sa, id, skip, tscale, lane);
+        stream_rows_lane<DTYPE, MODE, UNROLL>(g, sa, id, orow, tscale, lane);
 }
 
 // IDs only: the lookup kernel's first phase.  Each wave takes 64/H
@@ -449,8 +470,18 @@ __global__ __launch_bounds__(PLE_LOOKUP_BLOCK) void lookup_kernel(HashParams hp,
 __global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int32_t* __restrict__ tok,
                                                         const int32_t* __restrict__ qsl, int64_t T, int R,
                                                         const int32_t* __restrict__ ctx,
-                                                        int32_t* __restrict__ ids) {
+                                                        int32_t* __restrict__ ids, int id_blocks,
+                                                        int32_t* __restrict__ clear, int64_t clear_n,
+                                                        int32_t* __restrict__ zero, int zero_n) {
     __shared__ u32x4 head_lds[4][2 * kWave];
+    if ((int)blockIdx.x >= id_blocks) {  // the clearing blocks (no barriers in this kernel)
+        const int64_t nb = (int64_t)gridDim.x - id_blocks;
+        for (int64_t i = ((int64_t)blockIdx.x - id_blocks) * blockDim.x + threadIdx.x; i < clear_n;
+             i += nb * blockDim.x)
+            clear[i] = -1;
+        if (zero != nullptr && (int)blockIdx.x == id_blocks && (int)threadIdx.x < zero_n) zero[threadIdx.x] = 0;
+        return;
+    }
     const int lane = threadIdx.x & (kWave - 1);
     HeadStage hst;
     head_stage_load(hp, lane, hst);
@@ -460,7 +491,7 @@ __global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int
     const int TW = kWave / H;
     const int64_t nwaves = (T + TW - 1) / TW;
     for (int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wave < nwaves;
-         wave += (int64_t)gridDim.x * 4) {
+         wave += (int64_t)id_blocks * 4) {
         const int64_t t0 = wave * TW;
         const int nt = (int)min((int64_t)TW, T - t0);
         const bool active = lane < nt * H;
@@ -483,12 +514,19 @@ __global__ __launch_bounds__(256) void ngram_ids_kernel(HashParams hp, const int
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_ngram_ids(const HashParams& hp, const int32_t* tok, const int32_t* qsl, int64_t T, int R,
-                            const int32_t* ctx, int32_t* ids, hipStream_t s) {
+                            const int32_t* ctx, int32_t* ids, hipStream_t s, int32_t* clear, int64_t clear_n,
+                            int32_t* zero, int zero_n) {
     const int TW = kWave / hp.num_heads;
     const int64_t waves = (T + TW - 1) / TW;
     int64_t blocks = (waves + 3) / 4;
     if (blocks > (1 << 20)) blocks = 1 << 20;
-    hipLaunchKernelGGL(ngram_ids_kernel, dim3((unsigned)blocks), dim3(256), 0, s, hp, tok, qsl, T, R, ctx, ids);
+    int64_t clear_blocks = 0;
+    if (clear != nullptr || zero != nullptr) {
+        clear_blocks = (clear_n + 255) / 256;
+        clear_blocks = clear_blocks < 1 ? 1 : (clear_blocks > 1024 ? 1024 : clear_blocks);
+    }
+    hipLaunchKernelGGL(ngram_ids_kernel, dim3((unsigned)(blocks + clear_blocks)), dim3(256), 0, s, hp, tok, qsl, T, R,
+                       ctx, ids, (int)blocks, clear, clear_n, zero, zero_n < 0 ? 0 : (zero_n > 64 ? 64 : zero_n));
     return hipGetLastError();
 }
 
@@ -526,28 +564,34 @@ static hipError_t launch_lookup_t(const HashParams& hp, const LookupArgs& g, hip
                                              : (DTYPE == kFmtNVFP4 ? PLE_LOOKUP_LOADS_FP4 : PLE_LOOKUP_LOADS_FP8);
     const int64_t waves = (g.num_tokens + g.tokens_per_wave - 1) / g.tokens_per_wave;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    // the scalar-address stream needs rows of 64 x 2^k output chunks
-    const bool scalar_rows = g.cpr_log2 >= 6 && (DTYPE == kFmtBF16 ? PLE_LOOKUP_BF16_SCALAR_ROWS
-                                                                    : PLE_LOOKUP_QUANT_SCALAR_ROWS);
-    if (scalar_rows)
-        hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL, true>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK),
-                           0, s, hp, g);
-    else
-        hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL, false>), dim3((unsigned)blocks),
-                           dim3(PLE_LOOKUP_BLOCK), 0, s, hp, g);
+    // the scalar-address stream needs rows of 64 x 2^k output chunks (list
+    // mode writes each row to its own output row: the per-lane stream only)
+    if constexpr (MODE != kModeList) {
+        const bool scalar_rows =
+            g.cpr_log2 >= 6 && (DTYPE == kFmtBF16 ? PLE_LOOKUP_BF16_SCALAR_ROWS : PLE_LOOKUP_QUANT_SCALAR_ROWS);
+        if (scalar_rows) {
+            hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL, true>), dim3((unsigned)blocks),
+                               dim3(PLE_LOOKUP_BLOCK), 0, s, hp, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((lookup_kernel<DTYPE, MODE, UNROLL, false>), dim3((unsigned)blocks), dim3(PLE_LOOKUP_BLOCK), 0,
+                       s, hp, g);
     return hipGetLastError();
 }
 
+template <int DTYPE>
+static hipError_t launch_lookup_fmt(const HashParams& hp, const LookupArgs& g, int mode, hipStream_t s) {
+    if (mode == kModeHash) return launch_lookup_t<DTYPE, kModeHash>(hp, g, s);
+    if (mode == kModeList) return launch_lookup_t<DTYPE, kModeList>(hp, g, s);
+    return launch_lookup_t<DTYPE, kModeIds>(hp, g, s);
+}
+
 hipError_t launch_lookup(const HashParams& hp, const LookupArgs& g, int dtype, int mode, hipStream_t s) {
-    if (dtype == PLE_DTYPE_BF16)
-        return mode == kModeHash ? launch_lookup_t<kFmtBF16, kModeHash>(hp, g, s)
-                                 : launch_lookup_t<kFmtBF16, kModeIds>(hp, g, s);
-    if (dtype == PLE_DTYPE_NVFP4)
-        return mode == kModeHash ? launch_lookup_t<kFmtNVFP4, kModeHash>(hp, g, s)
-                                 : launch_lookup_t<kFmtNVFP4, kModeIds>(hp, g, s);
+    if (dtype == PLE_DTYPE_BF16) return launch_lookup_fmt<kFmtBF16>(hp, g, mode, s);
+    if (dtype == PLE_DTYPE_NVFP4) return launch_lookup_fmt<kFmtNVFP4>(hp, g, mode, s);
     // per-row and global-scale fp8 (the scale stride tells them apart)
-    return mode == kModeHash ? launch_lookup_t<kFmtFP8, kModeHash>(hp, g, s)
-                             : launch_lookup_t<kFmtFP8, kModeIds>(hp, g, s);
+    return launch_lookup_fmt<kFmtFP8>(hp, g, mode, s);
 }
 
 }  // namespace ple

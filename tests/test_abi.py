@@ -21,7 +21,7 @@ FAKE = 1 << 40  # a 256-aligned address that is never dereferenced: every call b
 
 def test_exports_every_header_function():
     names = capi.header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(capi._PROTOS)
@@ -180,9 +180,10 @@ def test_table_formats_rejected_before_any_launch():
 
 def test_dedup_workspace_size_and_limits():
     f = lib.ple_prefetch_dedup_workspace_bytes
-    # T*H = 24*4 = 96 rows: IDs and repeat map 96*4 bytes each (256-rounded), hash set of 256 slots x 2
-    assert f(24, 4) == 2 * 512 + 2 * 1024
-    assert f(8192, 8) == 2 * 65536 * 4 + 2 * 131072 * 4
+    # T*H = 24*4 = 96 rows: IDs, slots, list of distinct rows and list of repeats 96*4 bytes each
+    # (256-rounded), the lists' counts (256), hash set of 256 slots x 2 (keys, first position)
+    assert f(24, 4) == 4 * 512 + 256 + 2 * 1024
+    assert f(8192, 8) == 4 * 65536 * 4 + 256 + 2 * 131072 * 4
     assert f(0, 8) == 0 and f(1 << 22, 2) == 0  # beyond 2^22 rows: unsupported
     h, keep = _hash()
     layer = capi.ple_layer_desc(h, _table(), FAKE, 128, 1e-6, FAKE, 4, 2)
@@ -192,6 +193,18 @@ def test_dedup_workspace_size_and_limits():
     big = capi.ple_batch_desc(FAKE, FAKE, 1 << 21, 2, 0, None, None, None, None)
     assert lib.ple_prefetch_dedup(ctypes.byref(layer), ctypes.byref(big), FAKE, FAKE, 1 << 30, None, None) == E_UNSUP
     assert lib.ple_prefetch_dedup(None, ctypes.byref(b), FAKE, FAKE, 1 << 20, None, None) == E_ARG
+    # the two halves check the same things before any device call
+    assert lib.ple_prefetch_dedup_plan(ctypes.byref(layer), ctypes.byref(b), FAKE, 16, None) == E_WS
+    assert lib.ple_prefetch_dedup_plan(ctypes.byref(layer), ctypes.byref(big), FAKE, 1 << 30, None) == E_UNSUP
+    assert lib.ple_prefetch_dedup_plan(None, ctypes.byref(b), FAKE, 1 << 20, None) == E_ARG
+    assert lib.ple_prefetch_dedup_plan(ctypes.byref(layer), None, FAKE, 1 << 20, None) == E_ARG
+    assert lib.ple_prefetch_dedup_fetch(ctypes.byref(layer), b.num_tokens, FAKE + 4, 1 << 20, FAKE, None, None) == E_WS
+    assert lib.ple_prefetch_dedup_fetch(ctypes.byref(layer), b.num_tokens, FAKE, 1 << 20, FAKE + 2, None, None) == E_ARG
+    assert lib.ple_prefetch_dedup_fetch(ctypes.byref(layer), -1, FAKE, 1 << 20, FAKE, None, None) == E_ARG
+    assert lib.ple_prefetch_dedup_fetch(ctypes.byref(layer), 1 << 21, FAKE, 1 << 30, FAKE, None, None) == E_UNSUP
+    assert lib.ple_prefetch_dedup_fetch(None, b.num_tokens, FAKE, 1 << 20, FAKE, None, None) == E_ARG
+    # nothing to do: no device call
+    assert lib.ple_prefetch_dedup_fetch(ctypes.byref(layer), 0, None, 0, None, None, None) == 0
 
 
 def test_spec_commit_rejects_and_noops():
@@ -235,3 +248,25 @@ def test_prefill_noalloc_rejects_beyond_its_scratch():
     assert lib.ple_prefill_fused_noalloc(None, ctypes.byref(b), FAKE, None, FAKE, None, None) == E_ARG
     L2, keep2 = _layer(N=100)
     assert lib.ple_prefill_fused_noalloc(ctypes.byref(L2), ctypes.byref(b), FAKE, None, FAKE, None, None) == E_UNSUP
+
+
+def test_bench_library_exports_its_header():
+    """libple_bench (the benchmark's streaming-copy ceilings) loads and exports what
+    include/ple_bench.h declares; bad arguments are refused before any launch."""
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(root, "include", "ple_bench.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(ple_bench_[a-z_]+)\s*\(", text)))
+    assert names == ["ple_bench_copy", "ple_bench_copy_rows", "ple_bench_error_message"]
+    blib = ctypes.CDLL(os.path.join(root, "layer_embedding_lookup_amd", "libple_bench.so"))
+    for n in names:
+        assert hasattr(blib, n)
+    blib.ple_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    blib.ple_bench_copy_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert blib.ple_bench_copy(FAKE, FAKE + 256, 24, None) == E_ARG
+    assert blib.ple_bench_copy(FAKE + 8, FAKE + 256, 32, None) == E_ARG
+    assert blib.ple_bench_copy(FAKE, FAKE + 256, 0, None) == capi.PLE_OK
+    assert blib.ple_bench_copy_rows(FAKE, 10, 24, FAKE, 4, FAKE, None) == E_ARG
+    assert blib.ple_bench_copy_rows(FAKE, 10, 1024, FAKE, 0, FAKE, None) == capi.PLE_OK

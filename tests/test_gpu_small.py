@@ -803,9 +803,9 @@ def test_prefetch_dedup_equals_prefetch(variant):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8-global", "nvfp4"])
 def test_prefetch_dedup_rows_of_512(fmt):
-    """The deduplicating prefetch on 512-element rows (the scalar-address row stream for fp8 and NVFP4,
-    with the repeated rows skipped by its masked stores) equals the oracle's gather of the oracle's IDs
-    and the plain prefetch, bit for bit."""
+    """The deduplicating prefetch on 512-element rows in every table format (the list of distinct rows
+    walked by the per-lane row stream, then the repeats copied) equals the oracle's gather of the
+    oracle's IDs and the plain prefetch, bit for bit."""
     import dataclasses
     base = wl.CONFIGS[4] if fmt.startswith("fp8") else wl.CONFIGS[3]
     cfg = dataclasses.replace(base, idx=41, T=700, vocab_base=5003)
@@ -835,6 +835,39 @@ def test_prefetch_dedup_rows_of_512(fmt):
     np.testing.assert_array_equal(host_bits(staging), gather(ids).reshape(cfg.T, -1))
     assert torch.equal(staging.view(torch.int16), plain.view(torch.int16))
     assert int(nu.item()) == len(np.unique(ids)) < ids.size  # the Zipf batch repeats rows
+
+
+def test_prefetch_dedup_plan_fetch_on_two_streams():
+    """The two halves, the plan of the second layer on its own stream beside the first layer's fetch
+    (each layer its own workspace, the fetch ordered after its plan by an event), equal the oracle's
+    gather of each layer's oracle IDs, bit for bit, with the distinct-row counts."""
+    cfg = wl.CONFIGS[1]
+    b = wl.make_batch(cfg, layers=2, with_context=False)
+    L0, table, scales, kvw, cw, keep = _layer(cfg, b)
+    layers = [ple.Layer(hash_params(b, l), L0.table, L0.kv_weight, L0.conv_weight, conv_dilation=cfg.conv_dilation,
+                        eps=cfg.eps) for l in range(2)]
+    d_toks, d_qsl = dev(b.input_ids), dev(b.qsl)
+    need = ple.ple_prefetch_dedup_workspace_bytes(cfg.T, cfg.H)
+    ws = [torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    staging = [torch.full((cfg.T, cfg.H * cfg.D), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    nu = torch.full((2,), -1, dtype=torch.int32, device=DEV)
+    plan_s, fetch_s = torch.cuda.Stream(), torch.cuda.Stream()
+    planned = [torch.cuda.Event() for _ in range(2)]
+    torch.cuda.synchronize()
+    ple.ple_prefetch_dedup_plan(layers[0], d_toks, d_qsl, ws[0], stream=plan_s)
+    planned[0].record(plan_s)
+    fetch_s.wait_event(planned[0])
+    ple.ple_prefetch_dedup_fetch(layers[0], cfg.T, ws[0], staging[0], num_unique=nu[0:1], stream=fetch_s)
+    ple.ple_prefetch_dedup_plan(layers[1], d_toks, d_qsl, ws[1], stream=plan_s)
+    planned[1].record(plan_s)
+    fetch_s.wait_event(planned[1])
+    ple.ple_prefetch_dedup_fetch(layers[1], cfg.T, ws[1], staging[1], num_unique=nu[1:2], stream=fetch_s)
+    torch.cuda.synchronize()
+    for l in range(2):
+        ids = oracle.ngram_ids(b.input_ids, b.qsl, b.multipliers[l], b.vocab_sizes, b.offsets,
+                               context_len=cfg.context_len, heads_per_ngram=cfg.heads_per_ngram, eos_token_id=wl.EOS)
+        np.testing.assert_array_equal(host_bits(staging[l]), oracle.gather_bf16(table, ids).reshape(cfg.T, -1))
+        assert int(nu[l].item()) == len(np.unique(ids))
 
 
 def test_prefetch_dedup_empty_batch_counts_zero():
