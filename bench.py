@@ -216,23 +216,30 @@ def main() -> int:
     contig_ms = timed(bench_copy, 4 * L)
     contig_gbps = 2 * out_bytes / (contig_ms * 1e-3) / 1e9
     ids_rows = [ple.ple_ngram_ids(hashes[l], toks, qsl).view(-1) for l in range(L)]
-    row_copy_bytes = T * H * row_bytes_in
     rows_of_table = table.numel() * table.element_size() // row_bytes_in
 
+    # the random-row ceiling moves the lookup's own bytes: a bf16 table's rows
+    # copied as they are; a quantized table's codes widened to the 1 KiB
+    # output row, with its scale reads (per-row word, or NVFP4 block bytes)
+    expand = {"bf16": 1, "fp8": 2, "fp8-global": 2, "nvfp4": 4}[fmt]
+    aux_mode, aux_ptr = {"fp8": (1, tb.row_scales_ptr), "nvfp4": (2, tb.block_scales_ptr)}.get(fmt, (0, None))
+
     def bench_rows(i):
-        check_bench(blib.ple_bench_copy_rows(table.data_ptr(), rows_of_table, row_bytes_in,
-                                             ids_rows[i % L].data_ptr(), T * H, outs[i % len(outs)].data_ptr(),
-                                             torch.cuda.current_stream().cuda_stream), blib)
+        ids_p, out_p = ids_rows[i % L].data_ptr(), outs[i % len(outs)].data_ptr()
+        stream = torch.cuda.current_stream().cuda_stream
+        if fmt == "bf16":
+            check_bench(blib.ple_bench_copy_rows(table.data_ptr(), rows_of_table, row_bytes_in, ids_p, T * H, out_p,
+                                                 stream), blib)
+        else:
+            check_bench(blib.ple_bench_gather_expand(table.data_ptr(), rows_of_table, expand, aux_ptr, aux_mode,
+                                                     ids_p, T * H, D * 2, out_p, stream), blib)
     bench_rows(0)
     rows_ms = timed(bench_rows, 4 * L)
-    rows_gbps = (2 * row_copy_bytes + T * H * 4) / (rows_ms * 1e-3) / 1e9
+    rows_gbps = lookup_bytes_of(fmt, T, H, D, b.R) / (rows_ms * 1e-3) / 1e9
     del ids_rows
 
     R = b.R
-    # bytes read per (token, head) row: bf16 row; fp8 codes (+ the row's scale);
-    # NVFP4 codes + block scales
-    row_read = {"bf16": D * 2, "fp8": D + 4, "fp8-global": D, "nvfp4": D // 2 + D // 16}[fmt]
-    lookup_bytes = T * H * (row_read + D * 2) + T * 4 + (R + 1) * 4
+    lookup_bytes = lookup_bytes_of(fmt, T, H, D, R)
     lookup_gbps = lookup_bytes / (lookup_ms * 1e-3) / 1e9
     kv_flops = 2.0 * T * (H * D) * (2 * N)
     kv_tflops = kv_flops / (stage_ms["kv_proj"] * 1e-3) / 1e12
@@ -285,13 +292,24 @@ def main() -> int:
                         "conv": round(conv_bytes / (stage_ms["conv"] * 1e-3) / 1e9, 1)},
         "copy_ceiling": {"kernel": "hand-written 16-byte streaming copy (libple_bench), one pass per wave",
                          "random_rows_ms": round(rows_ms, 5), "random_rows_GBps": round(rows_gbps, 1),
-                         "random_rows": "the lookup's own rows (this batch's IDs, " + f"{row_bytes_in}-byte rows)",
+                         "random_rows": "the lookup's own rows and bytes (this batch's IDs, "
+                                        + f"{row_bytes_in}-byte table rows"
+                                        + ("" if fmt == "bf16" else " widened to 1 KiB, with the scale reads")
+                                        + "), no arithmetic",
                          "contiguous_ms": round(contig_ms, 5), "contiguous_GBps": round(contig_gbps, 1),
                          "bytes": out_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def lookup_bytes_of(fmt, T, H, D, R):
+    """Algorithmic bytes of one lookup: per (token, head) row the table row read
+    (bf16 row; fp8 codes and the row's scale; NVFP4 codes and block scales) and
+    the bf16 row written, plus the tokens and query_start_loc."""
+    row_read = {"bf16": D * 2, "fp8": D + 4, "fp8-global": D, "nvfp4": D // 2 + D // 16}[fmt]
+    return T * H * (row_read + D * 2) + T * 4 + (R + 1) * 4
 
 
 def bench_library():
@@ -304,6 +322,7 @@ def bench_library():
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.ple_bench_copy.argtypes = [P, P, ctypes.c_size_t, P]
     lib.ple_bench_copy_rows.argtypes = [P, I64, I32, P, I64, P, P]
+    lib.ple_bench_gather_expand.argtypes = [P, I64, I32, P, I32, P, I64, I32, P, P]
     lib.ple_bench_error_message.restype = ctypes.c_char_p
     return lib
 

@@ -34,6 +34,19 @@ int ple_bench_copy(const void* src, void* dst, size_t bytes, void* stream);
 int ple_bench_copy_rows(const void* src, int64_t src_rows, int32_t row_bytes, const int32_t* rows, int64_t nrows,
                         void* dst, void* stream);
 
+/*
+ * Row gather with the memory pattern of a quantized table's lookup, without
+ * its arithmetic: dst row k (out_row_bytes, a power of two in 32..16384) is
+ * src row rows[k] (out_row_bytes / expand bytes; expand 1, 2 or 4) repeated
+ * `expand` times, plus the table's side reads: aux_mode 0 none, 1 one 4-byte
+ * word per row (aux: [src_rows] words, the fp8 per-row scale), 2 one byte per
+ * 16 output elements (aux: [src_rows][out_row_bytes / 32] bytes, the NVFP4
+ * block scales).  The side value is XORed into each chunk, so its load
+ * counts.  1024 output chunks per wave, non-temporal loads and stores.
+ */
+int ple_bench_gather_expand(const void* src, int64_t src_rows, int32_t expand, const void* aux, int32_t aux_mode,
+                            const int32_t* rows, int64_t nrows, int32_t out_row_bytes, void* dst, void* stream);
+
 const char* ple_bench_error_message(void);
 
 #ifdef __cplusplus

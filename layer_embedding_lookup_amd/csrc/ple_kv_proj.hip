@@ -328,8 +328,15 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
 #pragma unroll
     for (int q = 0; q < 2 * NB; ++q) read_one(q, 0, 0, f0);
     for (int kt = 0; kt < nk; ++kt) slice(kt, f0, f1);
-    // the fragment reads above are opaque to the compiler's own waits
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // The last slice's look-ahead reads into f0 are still in flight and
+    // opaque to the compiler's own waits: this wait names f0's registers, so
+    // no epilogue value is placed in them before the reads have landed.
+    if constexpr (NB == 4)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : PLE_FRAG_REGS4(f0) : : "memory");
+    else if constexpr (NB == 2)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : PLE_FRAG_REGS2(f0) : : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : PLE_FRAG_REGS1(f0) : : "memory");
     __syncthreads();  // every wave is done with the stages before the epilogue reuses LDS
 
     // epilogue: acc[j][i][e] is feature n0 + wn*WT + j*32 + 8*(e/4) + 4*(lane/32) + e%4
@@ -478,7 +485,8 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         __builtin_amdgcn_sched_barrier(0);
         kstep(f1, f0, kt + 1, 0, kt + 2);
     }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // the last look-ahead reads into f0 land before its registers are reused
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" : PLE_FRAG8W_REGS(f0) : : "memory");
     __syncthreads();
 
     // acc[jb][ib][e]: feature n0 + wn*64 + jb*16 + 4*fk + e of token m0 + wm*128 + ib*16 + frow

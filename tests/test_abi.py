@@ -258,7 +258,7 @@ def test_bench_library_exports_its_header():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(root, "include", "ple_bench.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(ple_bench_[a-z_]+)\s*\(", text)))
-    assert names == ["ple_bench_copy", "ple_bench_copy_rows", "ple_bench_error_message"]
+    assert names == ["ple_bench_copy", "ple_bench_copy_rows", "ple_bench_error_message", "ple_bench_gather_expand"]
     blib = ctypes.CDLL(os.path.join(root, "layer_embedding_lookup_amd", "libple_bench.so"))
     for n in names:
         assert hasattr(blib, n)
@@ -270,3 +270,12 @@ def test_bench_library_exports_its_header():
     assert blib.ple_bench_copy(FAKE, FAKE + 256, 0, None) == capi.PLE_OK
     assert blib.ple_bench_copy_rows(FAKE, 10, 24, FAKE, 4, FAKE, None) == E_ARG
     assert blib.ple_bench_copy_rows(FAKE, 10, 1024, FAKE, 0, FAKE, None) == capi.PLE_OK
+    blib.ple_bench_gather_expand.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+    ge = blib.ple_bench_gather_expand
+    assert ge(FAKE, 10, 3, None, 0, FAKE, 4, 1024, FAKE, None) == E_ARG       # expand 1, 2 or 4
+    assert ge(FAKE, 10, 2, None, 1, FAKE, 4, 1024, FAKE, None) == E_ARG       # a side read needs aux
+    assert ge(FAKE, 10, 2, FAKE + 2, 1, FAKE, 4, 1024, FAKE, None) == E_ARG   # word-aligned aux
+    assert ge(FAKE, 10, 4, FAKE, 2, FAKE, 4, 1000, FAKE, None) == E_ARG       # power-of-two rows
+    assert ge(FAKE, 10, 4, FAKE, 2, FAKE, 0, 1024, FAKE, None) == capi.PLE_OK

@@ -388,6 +388,14 @@ CONV_CASES = [
     ([25, 3, 0, 40], 24, 6, 13, True),
     ([9, 70, 1], 8200, 4, 22, True),
     ([5, 90], 64, 16, 1, False),
+    # long requests (at least 4 d tokens each on average): the sliding-window
+    # kernel, with requests shorter than the dilation, empty requests, a
+    # partly filled last channel slice (N = 520) and kernel sizes 1-4
+    ([300, 1, 0, 257, 2, 140], 4096, 4, 3, True),
+    ([300, 1, 0, 257, 2, 140], 520, 3, 2, False),
+    ([500], 256, 2, 5, True),
+    ([97, 64, 161], 128, 1, 4, True),
+    ([1000, 23], 64, 4, 1, True),
 ]
 
 
@@ -447,13 +455,17 @@ def _oracle_chain(cfg, b, table, scales, kvw, cw, hidden, tokens=None, layer=0):
                           conv_state=b.conv_state, tokens=tokens)
 
 
-@pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2"])
+@pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2", "cfg1-long-state"])
 def test_prefill_fused_parity_small(variant):
     """The whole chain against the oracle's chain (out within 2e-2), and each stage against the oracle
     run on the GPU's own input to it: kv_proj on the gathered rows, the fp32 gate at rel 1e-5 on the
     GPU's kv (read from the workspace), the conv on the GPU's conv input."""
     cfg = wl.CONFIGS[2 if variant == "cfg2" else 1]
-    if variant == "cfg1-ctx-state":
+    if variant == "cfg1-long-state":
+        # long requests: the conv walks each residue class with a sliding window
+        import dataclasses
+        cfg = dataclasses.replace(cfg, idx=43, T=400, requests="fixed", fixed_lengths=(150, 1, 0, 97, 2, 150))
+    if variant in ("cfg1-ctx-state", "cfg1-long-state"):
         b = wl.make_batch(cfg, with_context=True, with_state=True)
     else:
         b = wl.make_batch(cfg)
