@@ -487,13 +487,145 @@ static hipError_t launch_conv_rows(const ConvRowsArgs& a, hipStream_t s) {
 
 bool conv_rows_supported(int K, int N) { return K >= 1 && K <= 4 && (size_t)N * K * 2 <= 64 * 1024; }
 
+// ---------------------------------------------------------------------------
+// LDS-staged conv for batches of long requests (prefill).  A block of four
+// waves takes TBS consecutive tokens x one 512-channel slice: it stages the
+// slice of rows t0-S .. t0+nt-1 in LDS once (gated, in the fused step: each
+// row multiplied by its token's gate once, not once per tap), every wave
+// with eight row loads in flight, then each wave forms the outputs of every
+// fourth token from the staged taps (the carried state's rows, for taps
+// before a request's start, straight from global memory).  The channel slice
+// varies fastest with the block id, so the slices of one token tile are
+// adjacent blocks.  Same arithmetic as conv_rows_kernel (gate_chunk,
+// conv_chunk), so the same bits.
+// ---------------------------------------------------------------------------
+#ifndef PLE_CONV_STAGED
+#define PLE_CONV_STAGED 1
+#endif
+#ifndef PLE_CONV_STAGED_TB
+#define PLE_CONV_STAGED_TB 16  // tokens per block (8, 12, 24, 32, 48 measured slower at the 8k prefill)
+#endif
+constexpr int kStageLoads = 8;   // staged rows in flight per wave
+
+template <int KC, int TBS, bool GATED>
+__global__ __launch_bounds__(256) void conv_staged_kernel(ConvRowsArgs a) {
+    extern __shared__ u32x4 s_x[];  // (TBS + S) rows x 64 chunks
+    __shared__ int32_t s_r[TBS];
+    __shared__ int64_t s_a[TBS];
+    __shared__ int64_t s_b[TBS];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid >> 6;
+    const int N = a.N;
+    const int nch = N >> 3;
+    const int nslice = (nch + kWave - 1) / kWave;
+    const int d = a.d;
+    const int S = (KC - 1) * d;
+    const int64_t t0 = (int64_t)(blockIdx.x / nslice) * TBS;
+    const int nt = (int)min((int64_t)TBS, a.T - t0);
+    const int c = (int)(blockIdx.x % nslice) * kWave + lane;
+    const bool cv = c < nch;
+    const int64_t coff = (int64_t)(cv ? c : nch - 1) * 8;  // lanes past the row stay in it
+    const int nrow = nt + S;
+
+    if (wv == 0) {
+        // the tile's tokens' requests (lane k: token t0 + k)
+        const int my_k = lane < nt ? lane : 0;
+        int r;
+        int64_t ra;
+        wave_find_request(a.qsl, a.R, t0 + my_k, t0, nt, my_k, lane, r, ra);
+        if (lane < nt) {
+            int64_t rb = a.qsl[r + 1];
+            rb = rb < t0 + my_k + 1 ? t0 + my_k + 1 : rb;
+            s_r[lane] = r;
+            s_a[lane] = ra;
+            s_b[lane] = rb;
+        }
+    }
+    // stage rows t0 - S + i (LDS row i), those before the batch as zeros
+    for (int i0 = wv; i0 < nrow; i0 += 4 * kStageLoads) {
+        u32x4 v[kStageLoads];
+        float g[kStageLoads];
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int i = i0 + 4 * u;
+            const int64_t p = t0 - S + i;
+            v[u] = u32x4{0u, 0u, 0u, 0u};
+            g[u] = 1.f;
+            if (i < nrow && p >= 0) {
+                v[u] = *(const u32x4*)(a.x + p * a.x_stride + coff);
+                if (GATED) g[u] = a.g[p];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int i = i0 + 4 * u;
+            if (i < nrow) s_x[i * kWave + lane] = GATED ? gate_chunk(g[u], v[u]) : v[u];
+        }
+    }
+    __syncthreads();
+    if (!cv) return;  // no barrier below
+
+    u32x4 wq[KC];
+#pragma unroll
+    for (int q = 0; q < KC; ++q) wq[q] = ((const u32x4*)a.w)[(int64_t)c * KC + q];
+    const int64_t S64 = S;
+    for (int k = wv; k < nt; k += 4) {
+        const int64_t t = t0 + k;
+        const int r = s_r[k];
+        const int64_t ra = s_a[k];
+        const int64_t rb = s_b[k];
+        u32x4 xv[KC];
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int64_t p = t - (int64_t)i * d;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (p >= ra)
+                v = s_x[(int)(p - (t0 - S)) * kWave + lane];
+            else if (a.state != nullptr)
+                v = *(const u32x4*)(a.state + ((int64_t)r * S64 + (S64 - (ra - p))) * N + coff);
+            xv[i] = v;
+        }
+#if PLE_CONV_NT_STORE
+        __builtin_nontemporal_store(conv_chunk<KC>(wq, xv), (u32x4*)(a.y + t * N + coff));
+#else
+        *(u32x4*)(a.y + t * N + coff) = conv_chunk<KC>(wq, xv);
+#endif
+        if (GATED && a.gated_out != nullptr && (t >= rb - S64 || rb - ra <= kConvInputWindow))
+            *(u32x4*)(a.gated_out + t * N + coff) = xv[0];
+    }
+}
+
+template <int KC, bool GATED>
+static hipError_t launch_conv_staged(const ConvRowsArgs& a, hipStream_t s) {
+    constexpr int TBS = PLE_CONV_STAGED_TB;
+    const int nslice = ((a.N >> 3) + kWave - 1) / kWave;
+    const size_t lds = (size_t)(TBS + (KC - 1) * a.d) * kWave * 16;
+    const int64_t blocks = (int64_t)nslice * ((a.T + TBS - 1) / TBS);
+    hipLaunchKernelGGL((conv_staged_kernel<KC, TBS, GATED>), dim3((unsigned)blocks), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+// Staging pays where a tile's tokens share their requests (prefill: requests
+// of 16 tokens and more on average) and the staged rows fit 64 KiB of LDS;
+// decode and verify windows keep one wave per token and row.
+static bool conv_staged_pays(const ConvRowsArgs& a, int K) {
+    return PLE_CONV_STAGED && a.R >= 1 && a.T >= (int64_t)16 * a.R && a.T >= 4 * PLE_CONV_STAGED_TB &&
+           (PLE_CONV_STAGED_TB + (int64_t)(K - 1) * a.d) * kWave * 16 <= 64 * 1024;
+}
+
+template <int KC, bool GATED>
+static hipError_t launch_conv_any(const ConvRowsArgs& a, hipStream_t s) {
+    return conv_staged_pays(a, KC) ? launch_conv_staged<KC, GATED>(a, s) : launch_conv_rows<KC, GATED>(a, s);
+}
+
 hipError_t launch_conv_gated(const ConvRowsArgs& a, int K, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
     switch (K) {
-        case 1: return launch_conv_rows<1, true>(a, s);
-        case 2: return launch_conv_rows<2, true>(a, s);
-        case 3: return launch_conv_rows<3, true>(a, s);
-        case 4: return launch_conv_rows<4, true>(a, s);
+        case 1: return launch_conv_any<1, true>(a, s);
+        case 2: return launch_conv_any<2, true>(a, s);
+        case 3: return launch_conv_any<3, true>(a, s);
+        case 4: return launch_conv_any<4, true>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -738,10 +870,10 @@ hipError_t launch_conv(const uint16_t* x, const int32_t* qsl, int64_t T, int R, 
         a.d = d;
         a.y = y;
         switch (K) {
-            case 1: return launch_conv_rows<1, false>(a, s);
-            case 2: return launch_conv_rows<2, false>(a, s);
-            case 3: return launch_conv_rows<3, false>(a, s);
-            default: return launch_conv_rows<4, false>(a, s);
+            case 1: return launch_conv_any<1, false>(a, s);
+            case 2: return launch_conv_any<2, false>(a, s);
+            case 3: return launch_conv_any<3, false>(a, s);
+            default: return launch_conv_any<4, false>(a, s);
         }
     }
     constexpr int TB = PLE_CONV_TOKENS_PER_BLOCK;
