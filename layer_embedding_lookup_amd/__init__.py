@@ -64,6 +64,21 @@ _BYTES = (torch.uint8, torch.int8)
 def _req(name: str, t, shape, dtypes, *, optional: bool = False):
     """Check one tensor argument: dtype, exact shape (None = any size on that
     axis), contiguity.  Returns the tensor."""
+    # fast path (these checks run on every call, and decode-sized calls are
+    # launch-bound): a well-formed tensor passes with a few attribute reads
+    if type(t) is torch.Tensor and t.dtype in dtypes:
+        ts = t.shape
+        if len(ts) == len(shape) and t.is_contiguous():
+            for got, want in zip(ts, shape):
+                if want is not None and got != want:
+                    break
+            else:
+                return t
+    return _req_checked(name, t, shape, dtypes, optional)
+
+
+def _req_checked(name: str, t, shape, dtypes, optional: bool):
+    """_req for anything the fast path did not pass: raises the precise error."""
     if t is None:
         if optional:
             return None
@@ -96,12 +111,17 @@ def _req_bytes(name: str, t, nbytes: int):
 
 def _same_device(*tensors):
     """Every tensor argument on one GPU (raw addresses and None are skipped)."""
-    devs = {(t.device.type, t.device.index) for t in tensors if isinstance(t, torch.Tensor)}
-    for typ, _ in devs:
-        if typ != "cuda":
-            raise ValueError("tensor arguments must be GPU tensors")
-    if len(devs) > 1:
-        raise ValueError(f"tensor arguments are on different devices: {sorted(devs)}")
+    dev = None
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            d = t.get_device()  # -1 for host tensors
+            if d < 0:
+                raise ValueError("tensor arguments must be GPU tensors")
+            if dev is None:
+                dev = d
+            elif d != dev:
+                devs = sorted({x.get_device() for x in tensors if isinstance(x, torch.Tensor)})
+                raise ValueError(f"tensor arguments are on different devices: {devs}")
 
 
 def _stream(stream) -> int | None:
@@ -126,10 +146,21 @@ class HashParams:
         self.first_head = int(first_head)
         self.num_heads = int(self.vocab_sizes.shape[0])
 
+    # The C descriptor is built once and rebuilt only after an attribute is
+    # reassigned (calls pass it by reference; the library only reads it).
+    def __setattr__(self, key, value):
+        object.__setattr__(self, key, value)
+        if key != "_desc":
+            object.__setattr__(self, "_desc", None)
+
     def desc(self) -> capi.ple_hash_desc:
-        return capi.ple_hash_desc(self.num_heads, self.heads_per_ngram, self.context_len, self.first_head,
-                                  self.eos_token_id, 0, self.multipliers.ctypes.data, self.vocab_sizes.ctypes.data,
-                                  self.offsets.ctypes.data)
+        d = self._desc
+        if d is None:
+            d = capi.ple_hash_desc(self.num_heads, self.heads_per_ngram, self.context_len, self.first_head,
+                                   self.eos_token_id, 0, self.multipliers.ctypes.data, self.vocab_sizes.ctypes.data,
+                                   self.offsets.ctypes.data)
+            object.__setattr__(self, "_desc", d)
+        return d
 
 
 class Table:
@@ -169,9 +200,18 @@ class Table:
         return cls(_ptr(codes), rows, 2 * half, PLE_DTYPE_NVFP4, _ptr(tensor_scale),
                    (codes, block_scales, tensor_scale), block_scales_ptr=_ptr(block_scales))
 
+    def __setattr__(self, key, value):
+        object.__setattr__(self, key, value)
+        if key != "_desc":
+            object.__setattr__(self, "_desc", None)
+
     def desc(self) -> capi.ple_table_desc:
-        return capi.ple_table_desc(self.ptr, self.num_rows, self.dim, self.dtype, self.row_scales_ptr,
-                                   self.block_scales_ptr)
+        d = self._desc
+        if d is None:
+            d = capi.ple_table_desc(self.ptr, self.num_rows, self.dim, self.dtype, self.row_scales_ptr,
+                                    self.block_scales_ptr)
+            object.__setattr__(self, "_desc", d)
+        return d
 
 
 class Layer:
@@ -188,9 +228,23 @@ class Layer:
         self.conv_dilation = int(conv_dilation)
         self.eps = float(eps)
 
+    def __setattr__(self, key, value):
+        object.__setattr__(self, key, value)
+        if key not in ("_desc", "_desc_parts", "_ws_bytes"):
+            object.__setattr__(self, "_desc", None)
+
     def desc(self) -> capi.ple_layer_desc:
-        return capi.ple_layer_desc(self.hash.desc(), self.table.desc(), _ptr(self.kv_weight), self.hidden,
-                                   self.eps, _ptr(self.conv_weight), self.conv_kernel, self.conv_dilation)
+        """The layer's C descriptor, rebuilt when an attribute (or the hash's or
+        table's descriptor) has changed; workspace sizes are cached with it."""
+        hd, td = self.hash.desc(), self.table.desc()
+        d = self._desc
+        if d is None or self._desc_parts[0] is not hd or self._desc_parts[1] is not td:
+            d = capi.ple_layer_desc(hd, td, _ptr(self.kv_weight), self.hidden, self.eps, _ptr(self.conv_weight),
+                                    self.conv_kernel, self.conv_dilation)
+            object.__setattr__(self, "_desc", d)
+            object.__setattr__(self, "_desc_parts", (hd, td))
+            object.__setattr__(self, "_ws_bytes", {})
+        return d
 
 
 def _batch(input_ids, query_start_loc, ngram_context=None, ngram_context_out=None, conv_state=None,
@@ -436,7 +490,11 @@ def ple_spec_commit(input_ids, query_start_loc, accepted, *, hash: HashParams = 
 
 def ple_prefill_workspace_bytes(layer: Layer, max_tokens: int) -> int:
     L = layer.desc()
-    return int(capi.load().ple_prefill_workspace_bytes(ctypes.byref(L), int(max_tokens)))
+    cache = layer._ws_bytes
+    n = cache.get(max_tokens)
+    if n is None:
+        n = cache[max_tokens] = int(capi.load().ple_prefill_workspace_bytes(ctypes.byref(L), int(max_tokens)))
+    return n
 
 
 def prefill_conv_input(layer: Layer, workspace, num_tokens: int):
