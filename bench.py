@@ -38,9 +38,11 @@ def log(msg: str) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20,
-                    help="untimed steps first (more than one rotation of the layers, so clocks and caches are settled)")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: past the chip's power-controller transient (after setup the clock "
+                         "boosts, then throttles below its steady value for about the first 50 prefill steps) and "
+                         "more than one rotation of the layers, so clocks and caches are settled")
     ap.add_argument("--layers", type=int, default=16, help="hash layers rotated over the steps")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--prefetch-cus", type=int, default=32, help="CUs of the host-table prefetch stream")
