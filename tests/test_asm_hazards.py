@@ -67,13 +67,17 @@ def _all_regs(text):
     return out
 
 
-def inline_lds_read_reuses(asm: str):
-    """(kernel, pending read, instruction) for each instruction that names a register an inline-asm
-    LDS read is still loading (in text order, up to the next lgkmcnt(0) wait)."""
-    found, kernel, pending, in_asm = [], None, {}, False
+def _blocks(asm: str):
+    """{kernel: [[label, [(in_asm, instruction)], [branch targets], falls_through]]}: each kernel's basic
+    blocks in text order, split at labels and after branches and s_endpgm."""
+    out, blocks, in_asm = {}, None, False
     for line in asm.splitlines():
         if re.match(r"^[A-Za-z_]\w*:", line):
-            kernel, pending = line.split(":")[0], {}
+            name = line.split(":")[0]
+            blocks = out.setdefault(name, [])
+            blocks.append([name, [], [], True])
+            continue
+        if blocks is None:
             continue
         if ";;#ASMSTART" in line:
             in_asm = True
@@ -82,18 +86,68 @@ def inline_lds_read_reuses(asm: str):
             in_asm = False
             continue
         text = line.split(";")[0].strip()
-        if not text or text.startswith(".") or text.endswith(":"):
+        if not text:
+            continue
+        if re.match(r"^\.L\w+:$", text):
+            blocks.append([text[:-1], [], [], True])
+            continue
+        if text.startswith("."):
             continue
         op = text.split()[0]
-        if op == "s_waitcnt" and "lgkmcnt(0)" in text:
-            pending = {}
-            continue
-        hit = _all_regs(text) & set(pending)
-        if hit:
-            found.append((kernel, pending[next(iter(hit))], text))
-        if in_asm and op.startswith("ds_read"):
-            for r in _all_regs(text.split()[1].rstrip(",")):
-                pending[r] = text
+        blocks[-1][1].append((in_asm, text))
+        if op.startswith("s_cbranch") or op == "s_branch":
+            blocks[-1][2].append(text.split()[1])
+            blocks[-1][3] = op != "s_branch"
+            blocks.append([None, [], [], True])
+        elif op in ("s_endpgm", "s_setpc_b64"):
+            blocks[-1][3] = False
+            blocks.append([None, [], [], True])
+    return out
+
+
+def inline_lds_read_reuses(asm: str):
+    """(kernel, pending read, instruction) for each instruction that names a register an inline-asm
+    LDS read may still be loading: one that no lgkmcnt(0) wait separates from the read on some path
+    through the kernel's branches (a forward data-flow over its basic blocks)."""
+    found = []
+    for kernel, blocks in _blocks(asm).items():
+        index = {b[0]: i for i, b in enumerate(blocks) if b[0]}
+        succ = []
+        for i, b in enumerate(blocks):
+            s = [index[t] for t in b[2] if t in index]
+            if b[3] and i + 1 < len(blocks):
+                s.append(i + 1)
+            succ.append(s)
+        entry = [{} for _ in blocks]
+
+        def walk(i, hits):
+            pending = dict(entry[i])
+            for in_asm, text in blocks[i][1]:
+                op = text.split()[0]
+                if op == "s_waitcnt" and "lgkmcnt(0)" in text:
+                    pending = {}
+                    continue
+                hit = _all_regs(text) & set(pending)
+                if hit and hits is not None:
+                    hits.append((kernel, pending[next(iter(hit))], text))
+                if in_asm and op.startswith("ds_read"):
+                    for r in _all_regs(text.split()[1].rstrip(",")):
+                        pending[r] = text
+            return pending
+
+        work = list(range(len(blocks)))
+        while work:  # the pending sets only grow, so this ends
+            i = work.pop()
+            for j in succ[i]:
+                grown = False
+                for r, t in walk(i, None).items():
+                    if r not in entry[j]:
+                        entry[j][r] = t
+                        grown = True
+                if grown:
+                    work.append(j)
+        for i in range(len(blocks)):
+            walk(i, found)
     return found
 
 
@@ -108,6 +162,22 @@ def test_scanners_find_the_patterns():
            "\tds_read_b128 v[30:33], v1\n\tv_mov_b32_e32 v30, 0\n")
     hits = inline_lds_read_reuses(asm)
     assert len(hits) == 1 and hits[0][2].startswith("v_add_u32_e32 v9")
+    # a loop body laid out before its header: the prologue's reads reach the body only through the
+    # header's wait, so reusing their registers there is fine
+    asm = ("k:\n\t;;#ASMSTART\n\tds_read_b128 v[8:11], v1\n\t;;#ASMEND\n\ts_branch .LBB0_2\n"
+           ".LBB0_1:\n\tv_mov_b32_e32 v8, 0\n.LBB0_2:\n\ts_waitcnt lgkmcnt(0)\n\ts_cbranch_scc1 .LBB0_1\n"
+           "\ts_endpgm\n")
+    assert inline_lds_read_reuses(asm) == []
+    # a read issued at the end of a loop body reaches the top of the body again over the back edge
+    asm = ("k:\n.LBB0_1:\n\tv_mov_b32_e32 v21, 0\n\ts_waitcnt lgkmcnt(0)\n\t;;#ASMSTART\n\tds_read_b128 "
+           "v[20:23], v1\n\t;;#ASMEND\n\ts_cbranch_scc1 .LBB0_1\n\ts_waitcnt lgkmcnt(0)\n\ts_endpgm\n")
+    hits = inline_lds_read_reuses(asm)
+    assert len(hits) == 1 and hits[0][2] == "v_mov_b32_e32 v21, 0", hits
+    # and one taken branch skipping the wait is enough
+    asm = ("j:\n\t;;#ASMSTART\n\tds_read_b128 v[8:11], v1\n\t;;#ASMEND\n\ts_cbranch_scc1 .LBB1_1\n"
+           "\ts_waitcnt lgkmcnt(0)\n.LBB1_1:\n\tv_mov_b32_e32 v9, 0\n\ts_endpgm\n")
+    hits = inline_lds_read_reuses(asm)
+    assert len(hits) == 1 and hits[0][2] == "v_mov_b32_e32 v9, 0", hits
 
 
 @pytest.fixture(scope="module")
