@@ -369,10 +369,17 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
 // (wm, wn) holds a 128 x 64 block (x rows wm*128.., W rows wn*64..) as 8 x 4
 // accumulator tiles of 16 x 16 (128 accumulation registers), so a wave
 // waiting on its fragments leaves the matrix core to the other wave of its
-// SIMD.  LDS layout, copies and slice pipeline as the four-wave body; a slice
-// is two K-steps of 32 with 12 fragment reads each.
+// SIMD.  Row layout in LDS and the copy instructions as the four-wave body; a
+// slice is two K-steps of 32 with 12 fragment reads each.  Instead of two
+// stages of both operands, the LDS holds a ring of five operand slices: with
+// every slot of one slice, the copy engine has more slack for the x panels,
+// which the XCD's L2 shares among fewer blocks (four) than the W panels
+// (eight), so more of their copies wait on the last-level cache.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 512;
+// five operand-slice slots (160 KiB, all of the LDS), which also hold the epilogue's rows
+constexpr int kWideLdsBytes = 5 * PipeShape<256>::OP_BYTES;
+static_assert(kWideLdsBytes >= PipeShape<256>::LDS_BYTES, "the epilogue's rows fit in the ring");
 struct Frag8w {
     u32x4 a[8], b[4];
 };
@@ -408,11 +415,17 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         boff[i] = (uint32_t)((min(n0 + row, O - 1) - n0) * K * 2 + kc * 16);
     }
     const int nk = K / kBBK;
-    auto copy_one = [&](int kt, int i) {
-        char* base = lds_raw + (kt & 1) * P::STAGE_BYTES + (i * 8 + wave) * 1024;
-        const int ko = min(kt, nk - 1) * kBBK * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)base, 16, aoff[i], ko, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + P::OP_BYTES), 16, boff[i], ko, 0, 0);
+    // Operand ring: x slice k in slot k mod 3, W slice k in slot 3 + k mod 2
+    // (slots of one operand slice, 32 KiB).  x slices are copied two slices
+    // ahead of their use and W slices one ahead, each into the slot its
+    // operand's slice three (x) or two (W) back has just left.
+    auto copy_x = [&](int k, int i) {  // k uniform
+        char* base = lds_raw + (k % 3) * P::OP_BYTES + (i * 8 + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)base, 16, aoff[i], min(k, nk - 1) * kBBK * 2, 0, 0);
+    };
+    auto copy_w = [&](int k, int i) {
+        char* base = lds_raw + (3 + (k & 1)) * P::OP_BYTES + (i * 8 + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)base, 16, boff[i], min(k, nk - 1) * kBBK * 2, 0, 0);
     };
 
     f32x4 acc[4][8];  // [W block jb][x block ib]
@@ -430,11 +443,11 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
     for (int ks = 0; ks < 2; ++ks) {
         const uint32_t col = (uint32_t)(((ks * 4 + fk) ^ sw) * 16);
         a_addr[ks] = lds_base + (wm * 128 + frow) * 128 + col;
-        b_addr[ks] = lds_base + P::OP_BYTES + (wn * 64 + frow) * 128 + col;
+        b_addr[ks] = lds_base + (wn * 64 + frow) * 128 + col;
     }
     auto read_one = [&](int q, int kt, int ks, Frag8w& f) {
-        const uint32_t so = (uint32_t)(kt & 1) * P::STAGE_BYTES;
-        const uint32_t pa = a_addr[ks] + so, pb = b_addr[ks] + so;
+        const uint32_t pa = a_addr[ks] + (uint32_t)(kt % 3) * P::OP_BYTES;
+        const uint32_t pb = b_addr[ks] + (uint32_t)(3 + (kt & 1)) * P::OP_BYTES;
         switch (q) {
             case 0: asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[0]) : "v"(pa)); break;
             case 1: asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(f.a[1]) : "v"(pa)); break;
@@ -451,12 +464,14 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         }
     };
     auto wait_frag = [&](Frag8w& f) { asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG8W_REGS(f)); };
+    // the wait leaves the NC copies of the newest x slice in flight (copies
+    // complete in issue order, so every older one has landed)
     auto wait_barrier = [&](Frag8w& f) {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG8W_REGS(f) : : "memory");
+        asm volatile("s_waitcnt vmcnt(%12) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG8W_REGS(f) : "i"(NC) : "memory");
     };
     // one K-step of 32: 32 MFMAs on cur; after MFMA t < 12, fragment read t of
-    // (rkt, rks) into nxt; with ckt >= 0, the NC copy pairs of slice ckt after
-    // MFMAs 2, 10, 18, 26
+    // (rkt, rks) into nxt; with ckt >= 0, the NC copies of W slice ckt after
+    // MFMAs 2 and 10, then those of x slice ckt + 1 after MFMAs 18 and 26
     auto kstep = [&](const Frag8w& cur, Frag8w& nxt, int rkt, int rks, int ckt) {
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
@@ -465,23 +480,37 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
                                                                 __builtin_bit_cast(bf16x8, cur.a[i]), acc[j][i], 0, 0,
                                                                 0);
             if (t < 12) read_one(t, rkt, rks, nxt);
-            if (ckt >= 0 && t % 8 == 2) copy_one(ckt, t / 8);
+            if (ckt >= 0 && t % 8 == 2) {
+                if (t < 16) {
+                    copy_w(ckt, 2 * (t / 8));
+                    copy_w(ckt, 2 * (t / 8) + 1);
+                } else {
+                    copy_x(ckt + 1, 2 * (t / 8) - 4);
+                    copy_x(ckt + 1, 2 * (t / 8) - 3);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     Frag8w f0, f1;
+    // x0, W0, x1, W1, x2; slice 0 landed before the first reads
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 2; ++k) {
 #pragma unroll
-        for (int i = 0; i < NC; ++i) copy_one(k, i);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"(2 * NC) : "memory");
+        for (int i = 0; i < NC; ++i) copy_x(k, i);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) copy_w(k, i);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) copy_x(2, i);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"(3 * NC) : "memory");
 #pragma unroll
     for (int q = 0; q < 12; ++q) read_one(q, 0, 0, f0);
     for (int kt = 0; kt < nk; ++kt) {
         wait_frag(f0);
         kstep(f0, f1, kt, 1, -1);
         __builtin_amdgcn_sched_barrier(0);
-        wait_barrier(f1);  // slice kt+1 has landed; every read of stage kt is done
+        wait_barrier(f1);  // slice kt+1 has landed; every read of slice kt is done
         __builtin_amdgcn_sched_barrier(0);
         kstep(f1, f0, kt + 1, 0, kt + 2);
     }
@@ -557,11 +586,10 @@ hipError_t launch_kv_proj(const uint16_t* x, const uint16_t* w, int64_t M, int K
     if (K > kBigMaxK) return hipErrorInvalidValue;  // rejected by the argument checks before this
     const int64_t big_tiles = ((M + 255) / 256) * ((O + 255) / 256);
     if (big_tiles >= 256) {
-        using P = PipeShape<256>;
         static const hipError_t attr = hipFuncSetAttribute((const void*)kv_proj_wide_kernel,
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS_BYTES);
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, kWideLdsBytes);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(kv_proj_wide_kernel, dim3((unsigned)big_tiles), dim3(kWideThreads), P::LDS_BYTES, s, x, w,
+        hipLaunchKernelGGL(kv_proj_wide_kernel, dim3((unsigned)big_tiles), dim3(kWideThreads), kWideLdsBytes, s, x, w,
                            (int)M, K, O, kv);
         return hipGetLastError();
     }
