@@ -275,7 +275,10 @@ def main() -> int:
         "roofline": {"kernel": "kv_proj (MFMA bf16 GEMM)", "bound": "mfma",
                      "achieved": round(kv_tflops, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kv_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic(cfg.name), "traffic_unit": "bytes per launch"},
+                     "traffic": recorded_traffic(cfg.name), "traffic_unit": "bytes per launch",
+                     "traffic_source": "profiles/kv_proj_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes "
+                                       "scaled by a contiguous copy's, recorded with the kernel source's hash "
+                                       "(null when the source has changed since)"},
         "lookup": {"kernel": "fused ids+gather" + ("" if fmt == "bf16" else f"+{fmt} dequant"),
                    "ms": round(lookup_ms, 5), "bytes": lookup_bytes,
                    "gathered_GBps": round(lookup_gbps, 1), "frac_hbm_peak": round(lookup_gbps / HBM_PEAK_GBPS, 4),
