@@ -22,6 +22,7 @@
 namespace ple {
 
 // Tile order: XCD-major then grouped row-major (GROUP_M tile rows share W panels).
+template <int GROUP_M>
 __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int total = tiles_m * tiles_n;
     // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -31,7 +32,6 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
         const int per = total >> 3;
         lin = (bid & 7) * per + (bid >> 3);
     }
-    constexpr int GROUP_M = 8;
     const int group = lin / (GROUP_M * tiles_n);
     const int first_m = group * GROUP_M;
     const int gm = min(tiles_m - first_m, GROUP_M);
@@ -137,7 +137,7 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
     const int tiles_m = (M + BT - 1) / BT;
     const int tiles_n = (O + BT - 1) / BT;
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_of_block<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BT, n0 = tn * BT;
 
     // Copy instruction i (0..NCOPY-1) of wave `wave` fills rows g*8 .. g*8+7
@@ -371,10 +371,11 @@ __device__ __forceinline__ void kv_proj_pipe(const uint16_t* __restrict__ x, con
 // waiting on its fragments leaves the matrix core to the other wave of its
 // SIMD.  Row layout in LDS and the copy instructions as the four-wave body; a
 // slice is two K-steps of 32 with 12 fragment reads each.  Instead of two
-// stages of both operands, the LDS holds a ring of five operand slices: with
-// every slot of one slice, the copy engine has more slack for the x panels,
-// which the XCD's L2 shares among fewer blocks (four) than the W panels
-// (eight), so more of their copies wait on the last-level cache.
+// stages of both operands, the LDS holds a ring of five operand slices, which
+// gives the W copies a second slice of lead.  The tiles an XCD runs at once
+// are grouped four tile rows by eight tile columns, so each W panel is shared
+// by four blocks in that XCD's L2 and each x panel by eight: more of the W
+// copies wait on the last-level cache.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 512;
 // five operand-slice slots (160 KiB, all of the LDS), which also hold the epilogue's rows
@@ -399,7 +400,7 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
     const int tiles_m = (M + BT - 1) / BT;
     const int tiles_n = (O + BT - 1) / BT;
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_of_block<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BT, n0 = tn * BT;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + (int64_t)m0 * K), (short)0, min(M - m0, BT) * K * 2, 0x00020000);
@@ -415,16 +416,16 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         boff[i] = (uint32_t)((min(n0 + row, O - 1) - n0) * K * 2 + kc * 16);
     }
     const int nk = K / kBBK;
-    // Operand ring: x slice k in slot k mod 3, W slice k in slot 3 + k mod 2
-    // (slots of one operand slice, 32 KiB).  x slices are copied two slices
-    // ahead of their use and W slices one ahead, each into the slot its
-    // operand's slice three (x) or two (W) back has just left.
+    // Operand ring: W slice k in slot k mod 3, x slice k in slot 3 + k mod 2
+    // (slots of one operand slice, 32 KiB).  W slices are copied two slices
+    // ahead of their use and x slices one ahead, each into the slot its
+    // operand's slice three (W) or two (x) back has just left.
     auto copy_x = [&](int k, int i) {  // k uniform
-        char* base = lds_raw + (k % 3) * P::OP_BYTES + (i * 8 + wave) * 1024;
+        char* base = lds_raw + (3 + (k & 1)) * P::OP_BYTES + (i * 8 + wave) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)base, 16, aoff[i], min(k, nk - 1) * kBBK * 2, 0, 0);
     };
     auto copy_w = [&](int k, int i) {
-        char* base = lds_raw + (3 + (k & 1)) * P::OP_BYTES + (i * 8 + wave) * 1024;
+        char* base = lds_raw + (k % 3) * P::OP_BYTES + (i * 8 + wave) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)base, 16, boff[i], min(k, nk - 1) * kBBK * 2, 0, 0);
     };
 
@@ -446,8 +447,8 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         b_addr[ks] = lds_base + (wn * 64 + frow) * 128 + col;
     }
     auto read_one = [&](int q, int kt, int ks, Frag8w& f) {
-        const uint32_t pa = a_addr[ks] + (uint32_t)(kt % 3) * P::OP_BYTES;
-        const uint32_t pb = b_addr[ks] + (uint32_t)(3 + (kt & 1)) * P::OP_BYTES;
+        const uint32_t pa = a_addr[ks] + (uint32_t)(3 + (kt & 1)) * P::OP_BYTES;
+        const uint32_t pb = b_addr[ks] + (uint32_t)(kt % 3) * P::OP_BYTES;
         switch (q) {
             case 0: asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[0]) : "v"(pa)); break;
             case 1: asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(f.a[1]) : "v"(pa)); break;
@@ -464,14 +465,14 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         }
     };
     auto wait_frag = [&](Frag8w& f) { asm volatile("s_waitcnt lgkmcnt(0)" : PLE_FRAG8W_REGS(f)); };
-    // the wait leaves the NC copies of the newest x slice in flight (copies
+    // the wait leaves the NC copies of the newest W slice in flight (copies
     // complete in issue order, so every older one has landed)
     auto wait_barrier = [&](Frag8w& f) {
         asm volatile("s_waitcnt vmcnt(%12) lgkmcnt(0)\n\ts_barrier" : PLE_FRAG8W_REGS(f) : "i"(NC) : "memory");
     };
     // one K-step of 32: 32 MFMAs on cur; after MFMA t < 12, fragment read t of
-    // (rkt, rks) into nxt; with ckt >= 0, the NC copies of W slice ckt after
-    // MFMAs 2 and 10, then those of x slice ckt + 1 after MFMAs 18 and 26
+    // (rkt, rks) into nxt; with ckt >= 0, the NC copies of x slice ckt after
+    // MFMAs 2 and 10, then those of W slice ckt + 1 after MFMAs 18 and 26
     auto kstep = [&](const Frag8w& cur, Frag8w& nxt, int rkt, int rks, int ckt) {
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
@@ -482,18 +483,18 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
             if (t < 12) read_one(t, rkt, rks, nxt);
             if (ckt >= 0 && t % 8 == 2) {
                 if (t < 16) {
-                    copy_w(ckt, 2 * (t / 8));
-                    copy_w(ckt, 2 * (t / 8) + 1);
+                    copy_x(ckt, 2 * (t / 8));
+                    copy_x(ckt, 2 * (t / 8) + 1);
                 } else {
-                    copy_x(ckt + 1, 2 * (t / 8) - 4);
-                    copy_x(ckt + 1, 2 * (t / 8) - 3);
+                    copy_w(ckt + 1, 2 * (t / 8) - 4);
+                    copy_w(ckt + 1, 2 * (t / 8) - 3);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     Frag8w f0, f1;
-    // x0, W0, x1, W1, x2; slice 0 landed before the first reads
+    // x0, W0, x1, W1, W2; slice 0 landed before the first reads
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -502,7 +503,7 @@ __device__ __forceinline__ void kv_proj_pipe8w(const uint16_t* __restrict__ x, c
         for (int i = 0; i < NC; ++i) copy_w(k, i);
     }
 #pragma unroll
-    for (int i = 0; i < NC; ++i) copy_x(2, i);
+    for (int i = 0; i < NC; ++i) copy_w(2, i);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"(3 * NC) : "memory");
 #pragma unroll
     for (int q = 0; q < 12; ++q) read_one(q, 0, 0, f0);
