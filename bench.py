@@ -238,6 +238,9 @@ def main() -> int:
     bench_rows(0)
     rows_ms = timed(bench_rows, 4 * L)
     rows_gbps = lookup_bytes_of(fmt, T, H, D, b.R) / (rows_ms * 1e-3) / 1e9
+    # rows that repeat within a batch are served by the caches: the distinct
+    # rows per layer, and the lookup's bytes counted with each row read once
+    distinct = float(np.mean([torch.unique(ids_rows[l]).numel() for l in range(L)]))
     del ids_rows
 
     R = b.R
@@ -289,7 +292,11 @@ def main() -> int:
                    "same_output_ms": round(lookup_same_ms, 5),
                    "same_output_frac_hbm_peak": round(lookup_bytes / (lookup_same_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                    "write_only_ms": round(write_only_ms, 5),
-                   "torch_index_select_ms": None if torch_gather_ms is None else round(torch_gather_ms, 5)},
+                   "torch_index_select_ms": None if torch_gather_ms is None else round(torch_gather_ms, 5),
+                   "distinct_rows": round(distinct, 1), "distinct_row_frac": round(distinct / (T * H), 4),
+                   "distinct_bytes": int(lookup_bytes - (T * H - distinct) * row_in_bytes(fmt, D)),
+                   "distinct_GBps": round((lookup_bytes - (T * H - distinct) * row_in_bytes(fmt, D))
+                                          / (lookup_ms * 1e-3) / 1e9, 1)},
         "kv_proj": {"ms": round(stage_ms["kv_proj"], 5), "ms_after_vendor": round(kv_again_ms, 5),
                     "torch_matmul_ms": round(vendor_kv_ms, 5), "flops": kv_flops},
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
@@ -309,12 +316,16 @@ def main() -> int:
     return 0
 
 
+def row_in_bytes(fmt, D):
+    """Bytes read per looked-up row: the bf16 row; fp8 codes and the row's
+    scale; NVFP4 codes and block scales."""
+    return {"bf16": D * 2, "fp8": D + 4, "fp8-global": D, "nvfp4": D // 2 + D // 16}[fmt]
+
+
 def lookup_bytes_of(fmt, T, H, D, R):
     """Algorithmic bytes of one lookup: per (token, head) row the table row read
-    (bf16 row; fp8 codes and the row's scale; NVFP4 codes and block scales) and
-    the bf16 row written, plus the tokens and query_start_loc."""
-    row_read = {"bf16": D * 2, "fp8": D + 4, "fp8-global": D, "nvfp4": D // 2 + D // 16}[fmt]
-    return T * H * (row_read + D * 2) + T * 4 + (R + 1) * 4
+    and the bf16 row written, plus the tokens and query_start_loc."""
+    return T * H * (row_in_bytes(fmt, D) + D * 2) + T * 4 + (R + 1) * 4
 
 
 def bench_library():
