@@ -528,18 +528,28 @@ __global__ __launch_bounds__(256) void conv_staged_kernel(ConvRowsArgs a) {
     const int64_t coff = (int64_t)(cv ? c : nch - 1) * 8;  // lanes past the row stay in it
     const int nrow = nt + S;
 
+    // Wave 0 finds the tile's tokens' requests (lane k: token t0 + k).  With
+    // fewer than 64 requests (one query_start_loc entry per lane) that entry
+    // goes out first and the wave's share of the staged rows right behind
+    // it, so the search costs no round trip of its own; more requests are
+    // searched before the staging, as their probe holds 16 registers.
+    const bool few_reqs = a.R + 1 <= kWave;
+    int q0 = 0;
     if (wv == 0) {
-        // the tile's tokens' requests (lane k: token t0 + k)
         const int my_k = lane < nt ? lane : 0;
-        int r;
-        int64_t ra;
-        wave_find_request(a.qsl, a.R, t0 + my_k, t0, nt, my_k, lane, r, ra);
-        if (lane < nt) {
-            int64_t rb = a.qsl[r + 1];
-            rb = rb < t0 + my_k + 1 ? t0 + my_k + 1 : rb;
-            s_r[lane] = r;
-            s_a[lane] = ra;
-            s_b[lane] = rb;
+        if (few_reqs) {
+            q0 = lane <= a.R ? a.qsl[lane] : 0;
+        } else {
+            int r;
+            int64_t ra;
+            wave_find_request(a.qsl, a.R, t0 + my_k, t0, nt, my_k, lane, r, ra);
+            if (lane < nt) {
+                int64_t rb = a.qsl[r + 1];
+                rb = rb < t0 + my_k + 1 ? t0 + my_k + 1 : rb;
+                s_r[lane] = r;
+                s_a[lane] = ra;
+                s_b[lane] = rb;
+            }
         }
     }
     // stage rows t0 - S + i (LDS row i), those before the batch as zeros
@@ -555,6 +565,26 @@ __global__ __launch_bounds__(256) void conv_staged_kernel(ConvRowsArgs a) {
             if (i < nrow && p >= 0) {
                 v[u] = *(const u32x4*)(a.x + p * a.x_stride + coff);
                 if (GATED) g[u] = a.g[p];
+            }
+        }
+        if (wv == 0 && i0 == 0 && few_reqs) {
+            // the request of token t0 + k: the entries qsl[1..R] at or below it
+            const int my_k = lane < nt ? lane : 0;
+            int r = 0;
+            for (int k = 0; k < nt; ++k) {
+                const uint64_t m = __ballot(lane >= 1 && lane <= a.R && (int64_t)q0 <= t0 + k);
+                const int rk = (int)__popcll(m);
+                if (k == my_k) r = rk < a.R - 1 ? rk : a.R - 1;
+            }
+            const int64_t t = t0 + my_k;
+            int64_t ra = __shfl(q0, r, kWave);
+            ra = ra < 0 ? 0 : (ra > t ? t : ra);
+            int64_t rb = __shfl(q0, r + 1, kWave);
+            rb = rb < t + 1 ? t + 1 : rb;
+            if (lane < nt) {
+                s_r[lane] = r;
+                s_a[lane] = ra;
+                s_b[lane] = rb;
             }
         }
 #pragma unroll
