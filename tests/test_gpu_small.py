@@ -455,17 +455,22 @@ def _oracle_chain(cfg, b, table, scales, kvw, cw, hidden, tokens=None, layer=0):
                           conv_state=b.conv_state, tokens=tokens)
 
 
-@pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2", "cfg1-long-state"])
+@pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2", "cfg1-long-state", "cfg1-k7-d2",
+                                     "cfg1-k12-d1"])
 def test_prefill_fused_parity_small(variant):
     """The whole chain against the oracle's chain (out within 2e-2), and each stage against the oracle
     run on the GPU's own input to it: kv_proj on the gathered rows, the fp32 gate at rel 1e-5 on the
-    GPU's kv (read from the workspace), the conv on the GPU's conv input."""
+    GPU's kv (read from the workspace), the conv on the GPU's conv input.  Conv kernels above 4 take the
+    entry point's other tail: the gate writes the gated value in full and the generic conv reads it."""
+    import dataclasses
     cfg = wl.CONFIGS[2 if variant == "cfg2" else 1]
     if variant == "cfg1-long-state":
         # long requests: the conv walks each residue class with a sliding window
-        import dataclasses
         cfg = dataclasses.replace(cfg, idx=43, T=400, requests="fixed", fixed_lengths=(150, 1, 0, 97, 2, 150))
-    if variant in ("cfg1-ctx-state", "cfg1-long-state"):
+    if variant.startswith("cfg1-k"):
+        K, d = int(variant.split("-k")[1].split("-")[0]), int(variant.split("-d")[1])
+        cfg = dataclasses.replace(cfg, idx=90 + K, conv_kernel=K, conv_dilation=d)
+    if variant in ("cfg1-ctx-state", "cfg1-long-state") or variant.startswith("cfg1-k"):
         b = wl.make_batch(cfg, with_context=True, with_state=True)
     else:
         b = wl.make_batch(cfg)
