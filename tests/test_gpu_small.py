@@ -396,6 +396,10 @@ CONV_CASES = [
     ([500], 256, 2, 5, True),
     ([97, 64, 161], 128, 1, 4, True),
     ([1000, 23], 64, 4, 1, True),
+    # the LDS-staged kernel's request search at 64 requests and more (the query_start_loc probe of up
+    # to 1024 requests, then the binary search beyond): 100 requests of 8-32 tokens, 1100 of 16
+    (list(range(8, 33)) * 4, 256, 4, 3, True),
+    ([16] * 1100, 64, 4, 3, True),
 ]
 
 
