@@ -96,6 +96,35 @@ def test_ids_edge_random(seed):
     np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
 
 
+def test_ids_and_rows_beyond_1024_requests():
+    """More than 1024 requests: the request search falls back from the query_start_loc probe to a
+    binary search (IDs, context out and rows against the oracle; 1500 requests of 0-8 tokens, a third of
+    them empty, with carried context)."""
+    rng = np.random.default_rng(77)
+    R, C, hpn = 1500, 2, 2
+    lens = rng.integers(0, 9, size=R)
+    lens[rng.random(R) < 0.33] = 0
+    qsl = wl.qsl_from_lengths(lens)
+    T = int(qsl[-1])
+    H = C * hpn
+    toks = rng.integers(0, 151936, size=T).astype(np.int32)
+    mult = rng.integers(-(1 << 63), (1 << 63) - 1, size=(H, C + 1), dtype=np.int64)
+    V = np.asarray([997, 1009, 1013, 1019], dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(V)[:-1]]).astype(np.int64)
+    ctx = rng.integers(0, 151936, size=(R, C)).astype(np.int32)
+    log(f"ids beyond 1024 requests: R={R} T={T}")
+    want, want_ctx = oracle.ngram_ids(toks, qsl, mult, V, off, context_len=C, heads_per_ngram=hpn,
+                                      eos_token_id=wl.EOS, ngram_context=ctx, want_context_out=True)
+    hp = ple.HashParams(mult, V, off, heads_per_ngram=hpn, context_len=C, eos_token_id=wl.EOS)
+    ctx_out = torch.full((R, C), -7, dtype=torch.int32, device=DEV)
+    got = ple.ple_ngram_ids(hp, dev(toks), dev(qsl), ngram_context=dev(ctx), ngram_context_out=ctx_out)
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+    np.testing.assert_array_equal(ctx_out.cpu().numpy(), want_ctx)
+    table = wl.normal_bf16((int(V.sum()), 64), 78, 0.02)
+    rows = ple.ple_lookup(hp, ple.Table.from_tensor(dev_bf16(table)), dev(toks), dev(qsl), ngram_context=dev(ctx))
+    np.testing.assert_array_equal(host_bits(rows), oracle.gather_bf16(table, want).reshape(T, -1))
+
+
 @pytest.mark.parametrize("seed", range(24))
 @pytest.mark.parametrize("fmt", ["bf16-32", "bf16-512", "fp8-512", "nvfp4-512"])
 def test_lookup_edge_random(seed, fmt):
