@@ -879,8 +879,10 @@ hipError_t launch_gate(const uint16_t* hidden, const uint16_t* kv, int64_t T, in
 
 hipError_t launch_gate_only(const uint16_t* hidden, const uint16_t* kv, int64_t T, int N, float eps, float* g,
                             float* gate, hipStream_t s) {
+    // passes of 4 chunks per lane: with fewer registers every wave of the 8k
+    // prefill is resident at once (the same sums in the same order as 8)
     const int64_t blocks = (T + 3) / 4;
-    hipLaunchKernelGGL((gate_kernel<8, false>), dim3((unsigned)blocks), dim3(256), 0, s, hidden, kv, T, N, eps,
+    hipLaunchKernelGGL((gate_kernel<4, false>), dim3((unsigned)blocks), dim3(256), 0, s, hidden, kv, T, N, eps,
                        nullptr, g, gate);
     return hipGetLastError();
 }
