@@ -429,6 +429,8 @@ CONV_CASES = [
     # to 1024 requests, then the binary search beyond): 100 requests of 8-32 tokens, 1100 of 16
     (list(range(8, 33)) * 4, 256, 4, 3, True),
     ([16] * 1100, 64, 4, 3, True),
+    # the per-row kernel (decode-shaped: about one token per request) beyond 1024 requests
+    ([1] * 1100 + [2, 0, 3], 256, 4, 3, True),
 ]
 
 
@@ -489,7 +491,7 @@ def _oracle_chain(cfg, b, table, scales, kvw, cw, hidden, tokens=None, layer=0):
 
 
 @pytest.mark.parametrize("variant", ["cfg1", "cfg1-ctx-state", "cfg2", "cfg1-long-state", "cfg1-k7-d2",
-                                     "cfg1-k12-d1"])
+                                     "cfg1-k12-d1", "cfg1-many-requests"])
 def test_prefill_fused_parity_small(variant):
     """The whole chain against the oracle's chain (out within 2e-2), and each stage against the oracle
     run on the GPU's own input to it: kv_proj on the gathered rows, the fp32 gate at rel 1e-5 on the
@@ -503,7 +505,12 @@ def test_prefill_fused_parity_small(variant):
     if variant.startswith("cfg1-k"):
         K, d = int(variant.split("-k")[1].split("-")[0]), int(variant.split("-d")[1])
         cfg = dataclasses.replace(cfg, idx=90 + K, conv_kernel=K, conv_dilation=d)
-    if variant in ("cfg1-ctx-state", "cfg1-long-state") or variant.startswith("cfg1-k"):
+    if variant == "cfg1-many-requests":
+        # 1100 requests of 0-2 tokens: the lookup's and the per-row conv's request searches fall back to
+        # a binary search beyond 1024 requests; every request carries context and conv state
+        lens = tuple(int(x) for x in np.random.default_rng(44).integers(0, 3, size=1100))
+        cfg = dataclasses.replace(cfg, idx=44, T=sum(lens), requests="fixed", fixed_lengths=lens)
+    if variant in ("cfg1-ctx-state", "cfg1-long-state", "cfg1-many-requests") or variant.startswith("cfg1-k"):
         b = wl.make_batch(cfg, with_context=True, with_state=True)
     else:
         b = wl.make_batch(cfg)
