@@ -565,7 +565,7 @@ def _run_fused_both(cfg, b, L, hidden, *, with_ctx, with_state, max_request_toke
 @pytest.mark.parametrize("case", ["decode-256", "decode-256-fresh", "tiny-empty-requests-k4", "tiny-k1", "tiny-k2",
                                   "tiny-k3-fresh", "all-empty", "windows-256x4", "windows-256x4-fresh",
                                   "tiny-windows-k4-d2", "tiny-windows-k2-d1", "tiny-windows-k3-d1-fresh",
-                                  "tiny-windows-k4-d3"])
+                                  "tiny-windows-k4-d3", "tiny-many-k4"])
 def test_decode_tail_equals_plain_path(case):
     """With max_request_tokens = 1..4 (decode steps, speculative verify windows) the fused entry point
     runs gate, conv and the carried state and context as one kernel; every output is the same bits as
@@ -589,6 +589,9 @@ def test_decode_tail_equals_plain_path(case):
         rng = np.random.default_rng(61 + K + 7 * d)
         if case == "all-empty":
             lens = [0, 0, 0]
+        elif "many" in case:
+            # 1100 requests of 0 or 1 tokens: past the 1024 requests the plain path's searches probe
+            lens = [int(x) for x in rng.integers(0, 2, size=1100)]
         elif "windows" in case:
             lens = [int(x) for x in rng.integers(0, 5, size=12)]
             lens[0], lens[1] = 4, 0
